@@ -1,0 +1,473 @@
+"""Pins for the CPU oracle (no GPU needed).
+
+Each test checks the oracle against something other than itself: values the
+pages print for a worked example, closed forms, invariants of the attention
+algebra, a brute-force per-token evaluation (tests/brute.py), and library
+routines (torch SDPA / autograd in float64 on the CPU).
+"""
+import copy
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- fixtures --
+
+def tiny_cases():
+    """Small varlen cases spanning every selection format, GQA, paging, causal
+    masks with Sq != Skv, ragged tails, zero-length sequences, messy index
+    lists (duplicates, unsorted, out of range, bad counts)."""
+    out = []
+    out.append(synth.random_case(11, lens_q=[37, 0, 50], lens_kv=[37, 5, 50], N1=2, D=8, bx=16, by=16,
+                                 kind="mask", density=0.5, dtype="f16"))
+    out.append(synth.random_case(12, lens_q=[40, 23], N1=4, N2=2, D=8, bx=16, by=8, kind="mask",
+                                 sparse_heads=2, causal=True, density=0.6))
+    out.append(synth.random_case(13, lens_q=[33, 17], lens_kv=[49, 9], N1=2, D=8, bx=8, by=16, kind="sabi",
+                                 causal=True, messy=True))
+    out.append(synth.random_case(14, lens_q=[30, 45], lens_kv=[20, 64], N1=4, N2=1, D=8, bx=16, by=16,
+                                 kind="idx", sparse_heads=1, messy=True, width=6))
+    out.append(synth.random_case(15, lens_q=[50, 31], lens_kv=[40, 70], N1=2, N2=2, D=8, bx=16, by=16,
+                                 kind="idx", causal=True, paged=True, page_size=16))
+    out.append(synth.random_case(16, lens_q=[29, 41], N1=2, D=8, bx=16, by=32, kind="none", causal=True))
+    out.append(synth.random_case(17, lens_q=[21], lens_kv=[35], N1=3, N2=3, D=8, bx=8, by=8, kind="none"))
+    out.append(synth.random_case(18, lens_q=[26, 19], N1=4, N2=2, D=8, bx=16, by=16, kind="sabi",
+                                 sparse_heads=4, paged=True, page_size=16, causal=False))
+    return out
+
+
+CASES = tiny_cases()
+
+
+def _f64(case):
+    """Copy of ``case`` with float64 Q/K/V/dO, for derivative checks."""
+    c = copy.copy(case)
+    for name in ("q", "k", "v", "dout"):
+        setattr(c, name, getattr(case, name).astype(np.float64))
+    return c
+
+
+# ------------------------------------------------------------ worked example --
+
+def test_allones_worked_example_lse_and_output():
+    fx = _load("blitz_allones_example.json")
+    S, N, D = fx["S"], fx["N"], fx["D"]
+    case = synth.ones_case(S=S, N=N, D=D, dtype=fx["dtype"], bx=fx["block_shape"][0], by=fx["block_shape"][1])
+    assert list(case.sparse.shape) == fx["sabi_shape"]
+    O, lse = oracle.forward(case)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=1e-12)
+    # The stated closed form ln S + sqrt(D), to the 4 decimals printed.
+    assert abs(lse[0, 0] - fx["expected_lse_stated"]) <= 0.5 * 10 ** -fx["expected_lse_stated_decimals"] + 1e-5
+    assert np.allclose(lse, math.log(S) + D * oracle.scale_of(0.0, D), rtol=0, atol=1e-9)
+    # The printed Ascend value, reproduced with the fp16-rounded scale.
+    fp16_scale = float(np.float16(1.0 / math.sqrt(D)))
+    case16 = synth.ones_case(S=S, N=N, D=D, dtype=fx["dtype"], scale=fp16_scale)
+    _, lse16 = oracle.forward(case16)
+    assert abs(lse16[0, 0] - fx["printed_lse0"]) <= 0.5 * 10 ** -fx["printed_lse0_decimals"]
+    # output[0] = 0x3C00 is fp16 1.0
+    assert np.float16(O[0, 0, 0]).view(np.uint16) == int(fx["printed_output0_bits"], 16)
+
+
+def test_sabi_example_shape_and_counts():
+    fx = _load("blitz_sabi_example.json")
+    S = fx["sequence_length"]
+    bx, by = fx["block_shape"]
+    assert -(-S // bx) == fx["num_rows"] and -(-S // by) == fx["num_cols"]
+    case = synth.ones_case(S=S, N=2, D=8, dtype="bf16", bx=bx, by=by)
+    sabi = np.full((1, 2, fx["num_rows"], fx["num_cols"]), 0xFFFF, dtype=np.uint16)
+    for r in fx["head0_rows_shown"]:
+        sabi[0, 0, r["row"]] = r["entries"]
+    case.sparse = sabi
+    idx = oracle.index_products(case, with_csc=False)
+    for r in fx["head0_rows_shown"]:
+        assert idx["counts"][r["row"]] == r["computes"]
+
+
+# ---------------------------------------------------- forward vs brute force --
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_forward_matches_brute_force(ci):
+    case = CASES[ci]
+    O, lse = oracle.forward(case)
+    Ob, lb = brute.dense_forward(case)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    assert np.array_equal(np.isinf(lse), np.isinf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_index_products_match_brute_force(ci):
+    case = CASES[ci]
+    idx = oracle.index_products(case)
+    pairs = brute.visited_pairs(case)
+    sq, skv = brute._lens(case)
+    nqb = [-(-s // case.bx) for s in sq]
+    nkb = [-(-s // case.by) for s in skv]
+    qbase = np.concatenate([[0], np.cumsum(nqb)]).astype(int)
+    kbase = np.concatenate([[0], np.cumsum(nkb)]).astype(int)
+    TQB, TKB = int(qbase[-1]), int(kbase[-1])
+    got = set()
+    rp, cols = idx["row_ptr"], idx["cols"]
+    for hs in range(case.sparse_heads):
+        for b in range(case.B):
+            for qb in range(nqb[b]):
+                r = hs * TQB + qbase[b] + qb
+                lst = cols[rp[r]:rp[r + 1]].tolist()
+                assert lst == sorted(set(lst))
+                got |= {(hs, b, qb, kb) for kb in lst}
+    assert got == pairs
+    # transpose relation and invariants
+    cp, qr = idx["col_ptr"], idx["qrows"]
+    assert rp[-1] == cp[-1]
+    got_t = set()
+    for hs in range(case.sparse_heads):
+        for b in range(case.B):
+            for kb in range(nkb[b]):
+                c = hs * TKB + kbase[b] + kb
+                lst = qr[cp[c]:cp[c + 1]].tolist()
+                assert lst == sorted(set(lst))
+                got_t |= {(hs, b, qb, kb) for qb in lst}
+    assert got_t == pairs
+    # work lists: permutations, non-increasing keys, ties by id
+    w = idx["work"]
+    cnt = np.diff(rp)
+    assert sorted(w.tolist()) == list(range(len(cnt)))
+    for a, b_ in zip(w[:-1], w[1:]):
+        assert cnt[a] > cnt[b_] or (cnt[a] == cnt[b_] and a < b_)
+    wk = idx["work_kv"]
+    key = idx["kv_key"]
+    assert sorted(wk.tolist()) == list(range(case.N2 * TKB))
+    for a, b_ in zip(wk[:-1], wk[1:]):
+        assert key[a] > key[b_] or (key[a] == key[b_] and a < b_)
+    # kv keys = number of (q-head pattern, q-block) pairs reaching each item
+    G = case.N1 // case.N2
+    for g in range(case.N2):
+        for b in range(case.B):
+            for kb in range(nkb[b]):
+                heads = [g] if case.sparse_heads == case.N2 else range(g * G, (g + 1) * G)
+                n = sum(1 for (hs, bb, qb, k2) in pairs if hs in heads and bb == b and k2 == kb)
+                assert key[g * TKB + kbase[b] + kb] == n
+
+
+def test_work_list_hand_example():
+    """Three rows with visited counts 1, 3, 1 and one empty row: work order
+    must be [1, 0, 2, 3] (descending count, ties by row id)."""
+    case = synth.random_case(3, lens_q=[64], N1=1, D=8, bx=16, by=16, kind="mask")
+    m = np.zeros((1, 1, 4, 4), dtype=np.uint8)
+    m[0, 0, 0, 0] = 1
+    m[0, 0, 1, [0, 2, 3]] = 1
+    m[0, 0, 2, 1] = 1
+    case.sparse = m
+    idx = oracle.index_products(case)
+    assert idx["row_ptr"].tolist() == [0, 1, 4, 5, 5]
+    assert idx["cols"].tolist() == [0, 0, 2, 3, 1]
+    assert idx["work"].tolist() == [1, 0, 2, 3]
+    assert idx["col_ptr"].tolist() == [0, 2, 3, 4, 5]
+    assert idx["qrows"].tolist() == [0, 1, 2, 1, 1]
+    assert idx["work_kv"].tolist() == [0, 1, 2, 3]
+
+
+def test_causal_bottom_right_visited_blocks():
+    """Sq=16, Skv=48, by=16 causal: query i sees keys j <= i + 32, so q-block 0
+    (rows 0..15) reaches blocks 0, 1, 2; with Sq=48, Skv=16 rows 0..31 see
+    nothing and the first two q-blocks are empty."""
+    c1 = synth.random_case(4, lens_q=[16], lens_kv=[48], N1=1, D=8, bx=16, by=16, kind="none", causal=True)
+    assert oracle.index_products(c1)["cols"].tolist() == [0, 1, 2]
+    c2 = synth.random_case(5, lens_q=[48], lens_kv=[16], N1=1, D=8, bx=16, by=16, kind="none", causal=True)
+    idx = oracle.index_products(c2)
+    assert idx["row_ptr"].tolist() == [0, 0, 0, 1]
+    O, lse = oracle.forward(c2)
+    assert np.all(np.isinf(lse[:32])) and np.all(O[:32] == 0)
+    assert np.all(np.isfinite(lse[32:]))
+
+
+# --------------------------------------------------------- library routines --
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_forward_matches_torch_sdpa(causal):
+    case = synth.random_case(21, lens_q=[45, 30], lens_kv=[45, 30], N1=2, N2=2, D=16, bx=16, by=16,
+                             kind="none", causal=causal)
+    O, lse = oracle.forward(case)
+    sg = oracle.scale_of(case.scale, case.D)
+    for b in range(case.B):
+        t0, t1 = int(case.cu_q[b]), int(case.cu_q[b + 1])
+        q = torch.from_numpy(case.q[t0:t1].astype(np.float64)).permute(1, 0, 2)
+        k = torch.from_numpy(case.k[t0:t1].astype(np.float64)).permute(1, 0, 2)
+        v = torch.from_numpy(case.v[t0:t1].astype(np.float64)).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=sg)
+        np.testing.assert_allclose(O[t0:t1], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def _torch_dense_grads(case):
+    """dq, dk, dv from torch autograd (float64, CPU) of dense attention masked
+    with the brute-force allowed matrix."""
+    sq, skv = brute._lens(case)
+    G = case.N1 // case.N2
+    sg = oracle.scale_of(case.scale, case.D)
+    dq = np.zeros(case.q.shape)
+    dk = np.zeros(case.k.shape)
+    dv = np.zeros(case.v.shape)
+    for b in range(case.B):
+        t0 = int(case.cu_q[b])
+        for h in range(case.N1):
+            g = h // G
+            A = torch.from_numpy(brute.token_allowed(case, b, h))
+            q = torch.from_numpy(case.q[t0:t0 + sq[b], h].astype(np.float64)).requires_grad_()
+            kk = torch.from_numpy(brute._keys(case, case.k, b, g)).requires_grad_()
+            vv = torch.from_numpy(brute._keys(case, case.v, b, g)).requires_grad_()
+            do = torch.from_numpy(case.dout[t0:t0 + sq[b], h].astype(np.float64))
+            s = (sg * q @ kk.T).masked_fill(~A, -math.inf)
+            has = A.any(dim=1, keepdim=True)
+            p = torch.softmax(torch.where(has, s, torch.zeros_like(s)), dim=1) * A * has
+            o = p @ vv
+            (o * do).sum().backward()
+            dq[t0:t0 + sq[b], h] = q.grad.numpy()
+            for j in range(skv[b]):
+                if case.paged:
+                    page = int(case.block_table[b, j // case.page_size])
+                    dk[page, j % case.page_size, g] += kk.grad[j].numpy()
+                    dv[page, j % case.page_size, g] += vv.grad[j].numpy()
+                else:
+                    dk[int(case.cu_kv[b]) + j, g] += kk.grad[j].numpy()
+                    dv[int(case.cu_kv[b]) + j, g] += vv.grad[j].numpy()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_backward_matches_torch_autograd(ci):
+    case = CASES[ci]
+    dq, dk, dv = oracle.backward(case)
+    rq, rk, rv = _torch_dense_grads(case)
+    np.testing.assert_allclose(dq, rq, rtol=0, atol=1e-11)
+    fin = ~np.isnan(case.k)  # paged tails hold NaN; their gradients stay 0
+    np.testing.assert_allclose(np.where(fin, dk, 0), np.where(fin, rk, 0), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(np.where(fin, dv, 0), np.where(fin, rv, 0), rtol=0, atol=1e-11)
+
+
+# ------------------------------------------------------- finite differences --
+
+def test_backward_finite_differences():
+    case = _f64(synth.random_case(31, lens_q=[19, 12], lens_kv=[23, 12], N1=2, N2=1, D=4, bx=8, by=8,
+                                  kind="mask", sparse_heads=2, causal=True, density=0.7))
+    dq, dk, dv = oracle.backward(case)
+    rng = np.random.default_rng(0)
+    h = 1e-6
+
+    def loss():
+        O, _ = oracle.forward(case)
+        return float((O * case.dout).sum())
+
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        arr = getattr(case, name)
+        for _ in range(12):
+            ix = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            old = arr[ix]
+            arr[ix] = old + h
+            lp = loss()
+            arr[ix] = old - h
+            lm = loss()
+            arr[ix] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[ix]) <= 1e-6 * max(1.0, abs(fd)), (name, ix, fd, grad[ix])
+
+
+# -------------------------------------------------------------- closed forms --
+
+def test_backward_allones_closed_form():
+    """All-ones inputs: dP = D = rowsum(dO o O), so dS = 0, dq = dk = 0, and
+    dv_j = sum over (h in group, i with j allowed) of 1/|A_i|."""
+    case = synth.random_case(41, lens_q=[40, 24], N1=4, N2=2, D=8, bx=16, by=8, kind="mask",
+                             sparse_heads=2, causal=True, density=0.6)
+    for name in ("q", "k", "v", "dout"):
+        setattr(case, name, np.ones_like(getattr(case, name)))
+    dq, dk, dv = oracle.backward(case)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    G = case.N1 // case.N2
+    expect = np.zeros(case.v.shape[:2])
+    for b in range(case.B):
+        for h in range(case.N1):
+            A = brute.token_allowed(case, b, h)
+            n = A.sum(axis=1)
+            for i in range(A.shape[0]):
+                if n[i]:
+                    for j in np.nonzero(A[i])[0]:
+                        expect[int(case.cu_kv[b]) + j, h // G] += 1.0 / n[i]
+    np.testing.assert_allclose(dv, np.repeat(expect[:, :, None], case.D, axis=2), rtol=0, atol=1e-12)
+
+
+def test_backward_invariants():
+    """sum_j dS_ij = 0 per row, hence (a) the key-gradient summed over each
+    sequence's keys vanishes and (b) dq = 0 when every key row of a head is
+    the same vector."""
+    case = _f64(synth.random_case(42, lens_q=[37, 22], lens_kv=[41, 30], N1=2, N2=2, D=8, bx=16, by=16,
+                                  kind="sabi", causal=True))
+    dq, dk, dv = oracle.backward(case)
+    for b in range(case.B):
+        k0, k1 = int(case.cu_kv[b]), int(case.cu_kv[b + 1])
+        s = dk[k0:k1].sum(axis=0)
+        assert np.abs(s).max() <= 1e-12 * max(1.0, np.abs(dk[k0:k1]).max())
+    case.k[:] = case.k[0:1]
+    dq2, _, _ = oracle.backward(case)
+    assert np.abs(dq2).max() <= 1e-12
+
+
+def test_empty_rows_and_unreached_keys():
+    case = synth.random_case(43, lens_q=[48], N1=1, D=8, bx=16, by=16, kind="mask")
+    m = np.zeros((1, 1, 3, 3), dtype=np.uint8)
+    m[0, 0, 0, 0] = 1
+    m[0, 0, 2, 0] = 1  # row 1 selects nothing; key block 1 and 2 unreached
+    case.sparse = m
+    O, lse = oracle.forward(case)
+    assert np.all(O[16:32] == 0) and np.all(np.isinf(lse[16:32])) and np.all(lse[16:32] > 0)
+    dq, dk, dv = oracle.backward(case)
+    assert np.all(dq[16:32] == 0)
+    assert np.all(dk[16:] == 0) and np.all(dv[16:] == 0)
+
+
+# ---------------------------------------------------------------- invariants --
+
+def test_rows_sum_to_one_via_unit_values():
+    """With V = 1 every non-empty row's output is sum_j P_ij = 1."""
+    for case in CASES:
+        c = copy.copy(case)
+        c.v = np.ones_like(case.v)
+        O, lse = oracle.forward(c)
+        ne = np.isfinite(lse)
+        np.testing.assert_allclose(O[ne], 1.0, rtol=0, atol=1e-12)
+
+
+def test_gqa_equals_repeated_mha():
+    case = synth.random_case(51, lens_q=[40, 27], N1=4, N2=2, D=8, bx=16, by=16, kind="mask",
+                             sparse_heads=2, causal=True, density=0.6)
+    G = 2
+    mha = copy.copy(case)
+    mha.N2 = 4
+    mha.sparse_heads = 4
+    mha.k = np.repeat(case.k, G, axis=1)
+    mha.v = np.repeat(case.v, G, axis=1)
+    mha.sparse = np.repeat(case.sparse, G, axis=1)
+    O1, l1 = oracle.forward(case)
+    O2, l2 = oracle.forward(mha)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+    dq1, dk1, dv1 = oracle.backward(case)
+    dq2, dk2, dv2 = oracle.backward(mha)
+    np.testing.assert_allclose(dq1, dq2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk1, dk2.reshape(dk2.shape[0], 2, G, -1).sum(2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv1, dv2.reshape(dv2.shape[0], 2, G, -1).sum(2), rtol=0, atol=1e-12)
+
+
+def test_paged_equals_packed():
+    case = CASES[4]
+    assert case.paged
+    packed = copy.copy(case)
+    packed.paged = False
+    lens = [int(x) for x in case.seqused_kv]
+    packed.cu_kv = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    ks, vs = [], []
+    for b, L in enumerate(lens):
+        for j in range(L):
+            page = int(case.block_table[b, j // case.page_size])
+            ks.append(case.k[page, j % case.page_size])
+            vs.append(case.v[page, j % case.page_size])
+    packed.k = np.stack(ks)
+    packed.v = np.stack(vs)
+    O1, l1 = oracle.forward(case)
+    O2, l2 = oracle.forward(packed)
+    assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+
+
+def test_varlen_equals_per_sequence():
+    case = CASES[1]
+    O, lse = oracle.forward(case)
+    for b in range(case.B):
+        one = copy.copy(case)
+        one.B = 1
+        t0, t1 = int(case.cu_q[b]), int(case.cu_q[b + 1])
+        k0, k1 = int(case.cu_kv[b]), int(case.cu_kv[b + 1])
+        one.cu_q = np.array([0, t1 - t0], dtype=np.int64)
+        one.cu_kv = np.array([0, k1 - k0], dtype=np.int64)
+        one.q, one.k, one.v = case.q[t0:t1], case.k[k0:k1], case.v[k0:k1]
+        one.sparse = case.sparse[b:b + 1]
+        O1, l1 = oracle.forward(one)
+        assert np.array_equal(O1, O[t0:t1]) and np.array_equal(l1, lse[t0:t1])
+
+
+def test_index_order_and_duplicates_irrelevant():
+    case = synth.random_case(61, lens_q=[40, 33], N1=2, D=8, bx=16, by=8, kind="idx", width=8)
+    O, lse = oracle.forward(case)
+    shuf = copy.copy(case)
+    idx = case.sparse.copy()
+    cnt = case.count.copy()
+    rng = np.random.default_rng(1)
+    for h in range(idx.shape[0]):
+        for r in range(idx.shape[1]):
+            n = int(cnt[h, r])
+            e = idx[h, r, :n].copy()
+            rng.shuffle(e)
+            if 0 < n < idx.shape[2]:
+                e = np.concatenate([e, e[:1]])  # duplicate an entry
+                cnt[h, r] = n + 1
+            idx[h, r, :len(e)] = e
+    shuf.sparse, shuf.count = idx, cnt
+    O2, l2 = oracle.forward(shuf)
+    assert np.array_equal(O, O2) and np.array_equal(lse, l2)
+
+
+def test_lse_merge_of_disjoint_block_sets():
+    """Splitting each row's selected blocks into X and Y: lse = logaddexp and
+    O is the lse-weighted mix (the partial-result merge the LSE output is for,
+    BlitzSparseAttention page, softmax_lse output)."""
+    case = synth.random_case(71, lens_q=[64, 48], N1=2, D=8, bx=16, by=16, kind="mask", density=0.8,
+                             causal=True)
+    X, Y = copy.copy(case), copy.copy(case)
+    cols = np.arange(case.sparse.shape[3])
+    X.sparse = case.sparse * (cols % 2 == 0)
+    Y.sparse = case.sparse * (cols % 2 == 1)
+    O, lse = oracle.forward(case)
+    Ox, lx = oracle.forward(X)
+    Oy, ly = oracle.forward(Y)
+    # an empty partial set stores lse = +inf; as a log-sum it is log(0) = -inf
+    lx = np.where(np.isinf(lx), -np.inf, lx)
+    ly = np.where(np.isinf(ly), -np.inf, ly)
+    lm = np.logaddexp(lx, ly)
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lm[fin], lse[fin], rtol=0, atol=1e-12)
+    with np.errstate(invalid="ignore"):
+        wx = np.where(np.isfinite(lx), np.exp(lx - lm), 0.0)
+        wy = np.where(np.isfinite(ly), np.exp(ly - lm), 0.0)
+    mix = wx[..., None] * Ox + wy[..., None] * Oy
+    np.testing.assert_allclose(mix[fin], O[fin], rtol=0, atol=1e-12)
+
+
+def test_config_structures():
+    """Structural facts of the benchmark workloads: exact visited-pair count
+    of the long-context mask and shapes of the other selection tensors."""
+    c5 = synth.config5(values=False)
+    assert c5.sparse.shape == (2, 16, 128, 128)
+    per_row = c5.sparse.sum(axis=3)
+    expect = np.array([min(i + 1, 13) for i in range(128)])
+    assert np.array_equal(per_row, np.broadcast_to(expect, per_row.shape))
+    assert int(per_row.sum()) == 50752 // 1  # visited (b, h, qb, kb) pairs
+    c3 = synth.config3(values=False)
+    assert c3.sparse.shape == (1, 32, 256, 64) and c3.sparse.dtype == np.uint16
+    n = (c3.sparse != 0xFFFF).sum(axis=3)
+    assert n.min() >= 1 and n.max() <= 16
+    c4 = synth.config4(values=False)
+    assert c4.sparse.shape[0] == 8 and c4.sparse.shape[2] == 16
+    assert c4.count.min() >= 1 and c4.count.max() <= 16
