@@ -1,0 +1,169 @@
+// Device helpers for the gfx950 kernels: MFMA operand types, fp32 -> 16-bit
+// packing, LDS tile addressing and wave-level utilities.
+//
+// MFMA v_mfma_f32_32x32x16_{bf16,f16} lane layout (wave64), checked on the
+// hardware:
+//   A (32 x 16, M x K): lane l holds row l % 32, k = 8 * (l / 32) + j, j < 8
+//   B (16 x 32, K x N): lane l holds col l % 32, k = 8 * (l / 32) + j
+//   C (32 x 32):        lane l, element i holds row 8 * (i / 4) + 4 * (l / 32)
+//                       + i % 4 of column l % 32
+// ds_read_b64_tr_b16: within each 16-lane group, lane i returns element i % 4
+// of the 8-byte rows addressed by source lanes i / 4 + 4 j (j < 4).  With
+// source lane s pointing at row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3 of a
+// row-major 16-bit matrix, lane i receives rows r0 .. r0 + 3 of column c0 + i:
+// a transposed operand read straight from a row-major LDS tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+struct BF16 {
+  typedef bf16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+  // Two fp32 values rounded to nearest-even bf16, packed lo | hi << 16.
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2_t r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+};
+
+struct F16 {
+  typedef f16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2_t r;
+    r[0] = (_Float16)lo;
+    r[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+  }
+};
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// Row-major LDS tiles of 16-bit elements, `D` columns per row, stored in
+// 16-byte chunks whose position inside the row is XOR-permuted by the row
+// index so that the MFMA operand reads (32 rows at one chunk, or 8 rows x 4
+// chunks for the transposed reads) spread over the LDS banks.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Tile {
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (CH == 16) {
+      return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+      return row & (CH - 1);
+    }
+  }
+  // byte offset of 16-byte chunk `c` of `row`
+  static __device__ __forceinline__ int chunk_off(int row, int c) {
+    return row * ROW_BYTES + ((c ^ swz(row)) << 4);
+  }
+  // byte offset of column `col` (multiple of 4) of `row`
+  static __device__ __forceinline__ int col_off(int row, int col) {
+    return row * ROW_BYTES + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
+  }
+};
+
+__device__ __forceinline__ u32x4_t lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4_t*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(char* base, int off, const u32x4_t& v) {
+  *reinterpret_cast<u32x4_t*>(base + off) = v;
+}
+// Transposed read: see the layout note at the top of the file.
+__device__ __forceinline__ u32x2_t lds_read_tr(const char* base, int off) {
+  i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+__device__ __forceinline__ u32x4_t gload16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x4_t zero_u4() {
+  u32x4_t z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+// Paged or packed location of a key row: element offset of (key, head g, 0).
+struct KvAddr {
+  const int32_t* block_table;
+  int64_t seq_row0;     // TND: cu_kv[b]; unused when paged
+  int64_t page_stride;  // elements
+  int32_t bt_row;       // b * max_pages
+  int32_t page_size;
+  int32_t paged;
+  int64_t row_stride;   // N2 * D
+  int64_t head_off;     // g * D
+  __device__ __forceinline__ int64_t offset(int key) const {
+    if (paged) {
+      const int page = block_table[bt_row + key / page_size];
+      return (int64_t)page * page_stride + (int64_t)(key % page_size) * row_stride + head_off;
+    }
+    return (seq_row0 + key) * row_stride + head_off;
+  }
+};
+
+}  // namespace bsa

@@ -1,0 +1,443 @@
+// Block-index preprocessor: turns the per-q-block KV-block selection into the
+// schedule the attention kernels walk.
+//
+//  * rows r = hs * totalQBlocks + qbase_b + qb (head-major over global q-blocks,
+//    the order of GenericBlockSparseAttention's [N2, totalQBlocks, topK]
+//    sparseBlockIdx tensor);
+//  * CSR row_ptr/cols: per row the ascending local KV blocks that hold at least
+//    one allowed (query, key) pair -- the selected set (block mask, 0xFFFF
+//    padded sabi, or -1 padded idx with count; BlockSparseAttentionGrad README,
+//    BlitzSparseAttention sabi section, GenericBlockSparseAttention parameter
+//    table) de-duplicated, restricted to [0, nKB_b) and cut by the causal mask;
+//  * work: rows by visited count descending, ties by row id (longest first for
+//    load balance, the role of GenericBlockSparseAttention's metadata
+//    pre-operator);
+//  * CSC col_ptr/qrows: per KV block the ascending q-blocks that visit it (the
+//    per-KV-block layout of GenericBlockSparseAttention's layoutSparsePattern
+//    table), and work_kv: dK/dV items by load, descending.
+//
+// Every product is deterministic: counts come from LDS bitmaps and atomics
+// whose results do not depend on order, the scans are sequential per block,
+// orders come from a stable LSD radix sort, and column lists are re-sorted
+// through bitmaps after their order-dependent atomic fill.
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+namespace {
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ int seq_kv_len(const SeqArgs& s, int b) {
+  if (s.seqused_kv) return s.seqused_kv[b];
+  return (int)(s.cu_kv[b + 1] - s.cu_kv[b]);
+}
+
+// Block-wide inclusive scan of one int per thread (blockDim.x == 256 or 1024).
+template <int NT>
+__device__ int block_incl_scan(int x, int* wsum, int& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = wave_incl_scan(x);
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int v = wsum[i];
+    if (i < w) off += v;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return inc + off;
+}
+
+// ------------------------------------------------------------------ setup --
+// One block: per-sequence lengths, q/kv block bases, block -> sequence maps,
+// header.
+__global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs, int n2) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x;
+  const int B = seq.batch;
+  int carry_q = 0, carry_k = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    int nq = 0, nk = 0;
+    if (b < B) {
+      const int sq = (int)(seq.cu_q[b + 1] - seq.cu_q[b]);
+      const int skv = seq_kv_len(seq, b);
+      ip.sq[b] = sq;
+      ip.skv[b] = skv;
+      nq = cdiv(sq, seq.bx);
+      nk = cdiv(skv, seq.by);
+    }
+    int tq, tk;
+    const int iq = block_incl_scan<256>(nq, wsum, tq);
+    const int ik = block_incl_scan<256>(nk, wsum, tk);
+    if (b < B) {
+      ip.qbase[b] = carry_q + iq - nq;
+      ip.kbase[b] = carry_k + ik - nk;
+    }
+    carry_q += tq;
+    carry_k += tk;
+  }
+  if (tid == 0) {
+    ip.qbase[B] = carry_q;
+    ip.kbase[B] = carry_k;
+    ip.hdr[H_TQB] = carry_q;
+    ip.hdr[H_TKB] = carry_k;
+    ip.hdr[H_R] = hs * carry_q;
+    ip.hdr[H_C] = hs * carry_k;
+    ip.hdr[H_NNZ] = 0;
+    ip.hdr[H_KVITEMS] = n2 * carry_k;
+    for (int i = H_KVITEMS + 1; i < H_COUNT; ++i) ip.hdr[i] = 0;
+  }
+  __syncthreads();
+  for (int b = 0; b < B; ++b) {
+    const int q0 = ip.qbase[b], q1 = ip.qbase[b + 1];
+    for (int x = q0 + tid; x < q1; x += 256) ip.qb_seq[x] = b;
+    const int k0 = ip.kbase[b], k1 = ip.kbase[b + 1];
+    for (int x = k0 + tid; x < k1; x += 256) ip.kb_seq[x] = b;
+  }
+}
+
+// ------------------------------------------------------- row visited sets --
+// Builds, in the calling wave's LDS words, the bitmap of row r's visited KV
+// blocks and returns the number of bit positions in use (0 for r >= R).  All
+// four waves of the block call it together (it contains block barriers).
+__device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, const IndexPtrs& ip,
+                          int r, int R, int TQB) {
+  const int lane = lane_id();
+  int nbits = 0, b = 0, qb = 0, hs = 0, qg = 0;
+  if (r < R) {
+    hs = r / TQB;
+    qg = r - hs * TQB;
+    b = ip.qb_seq[qg];
+    qb = qg - ip.qbase[b];
+    const int sq = ip.sq[b], skv = ip.skv[b];
+    const int last_row = min((qb + 1) * seq.bx, sq) - 1;
+    int lim = skv - 1;  // largest allowed key of the q-block's last row
+    if (seq.causal) lim = min(lim, last_row + skv - sq);
+    nbits = lim < 0 ? 0 : lim / seq.by + 1;
+  }
+  const int nwords = (nbits + 31) >> 5;
+  for (int w = lane; w < nwords; w += 64) {
+    uint32_t v = 0;
+    if (sel.kind == SP_NONE) {
+      const int hi = nbits - w * 32;
+      v = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+    }
+    bm[w] = v;
+  }
+  __syncthreads();
+  if (nbits > 0 && sel.kind != SP_NONE) {
+    if (sel.kind == SP_MASK || sel.kind == SP_SABI) {
+      if (qb < sel.rows) {
+        const int64_t row = (((int64_t)b * sel.hs + hs) * sel.rows + qb) * sel.width;
+        if (sel.kind == SP_MASK) {
+          const uint8_t* m = reinterpret_cast<const uint8_t*>(sel.sparse) + row;
+          const int n = min(sel.width, nbits);
+          for (int kb = lane; kb < n; kb += 64)
+            if (m[kb]) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+        } else {
+          const uint16_t* s = reinterpret_cast<const uint16_t*>(sel.sparse) + row;
+          for (int t = lane; t < sel.width; t += 64) {
+            const int kb = s[t];
+            if (kb != 0xFFFF && kb < nbits) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+          }
+        }
+      }
+    } else {  // SP_IDX over global q-blocks
+      if (qg < sel.rows) {
+        const int64_t rr = (int64_t)hs * sel.rows + qg;
+        const int n = min(max(sel.count[rr], 0), sel.width);
+        const int32_t* ix = reinterpret_cast<const int32_t*>(sel.sparse) + rr * sel.width;
+        for (int t = lane; t < n; t += 64) {
+          const int kb = ix[t];
+          if (kb >= 0 && kb < nbits) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return nbits;
+}
+
+__global__ __launch_bounds__(256) void k_row_count(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t rbar,
+                                                   int words, int cmax) {
+  extern __shared__ uint32_t smem_bm[];
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  uint32_t* bm = smem_bm + wv * words;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB];
+  const int nbits = row_bitmap(bm, seq, sel, ip, r < rbar ? (int)r : R, R, TQB);
+  int cnt = 0;
+  for (int w = lane; w < ((nbits + 31) >> 5); w += 64) cnt += __popc(bm[w]);
+  cnt = wave_sum_i(cnt);
+  if (lane == 0 && r < rbar) {
+    ip.row_cnt[r] = cnt;
+    ip.key0[r] = r < R ? cmax - cnt : cmax + 1;
+    ip.val0[r] = (int)r;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t rbar, int words) {
+  extern __shared__ uint32_t smem_bm[];
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  uint32_t* bm = smem_bm + wv * words;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB];
+  const int nbits = row_bitmap(bm, seq, sel, ip, r < rbar ? (int)r : R, R, TQB);
+  if (r >= R) return;
+  const int nwords = (nbits + 31) >> 5;
+  int pos = ip.row_ptr[r];
+  for (int c = 0; c < nwords; c += 64) {
+    const int w = c + lane;
+    uint32_t word = w < nwords ? bm[w] : 0u;
+    const int pc = __popc(word);
+    const int inc = wave_incl_scan(pc);
+    int o = pos + inc - pc;
+    while (word) {
+      const int bit = __ffs(word) - 1;
+      ip.cols[o++] = w * 32 + bit;
+      word &= word - 1;
+    }
+    pos += __shfl(inc, 63, 64);
+  }
+}
+
+// --------------------------------------------------------- exclusive scan --
+// out[0..n) = exclusive prefix sums of in[0..n), out[n] = total; also copies
+// the total to *total_out when given.  One block of 1024 threads.
+__global__ __launch_bounds__(1024) void k_scan_excl(const int32_t* in, int32_t* out, int64_t n, int32_t* total_out) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int64_t base = 0; base < n; base += 4096) {
+    int v[4];
+    int s = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = base + tid * 4 + e;
+      v[e] = i < n ? in[i] : 0;
+      s += v[e];
+    }
+    int tot;
+    const int inc = block_incl_scan<1024>(s, wsum, tot);
+    int run = carry + inc - s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = base + tid * 4 + e;
+      if (i < n) out[i] = run;
+      run += v[e];
+    }
+    carry += tot;
+  }
+  if (tid == 0) {
+    out[n] = carry;
+    if (total_out) *total_out = carry;
+  }
+}
+
+// ---------------------------------------------------- stable radix sort ----
+// LSD radix sort on 8-bit digits of non-negative keys; each pass is stable,
+// so equal keys keep their input (id) order.
+__global__ __launch_bounds__(256) void k_radix_hist(const int32_t* key, int64_t n, int shift, int32_t* hist,
+                                                    int nblocks) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+  if (i < n) atomicAdd(&h[(key[i] >> shift) & 255], 1);
+  __syncthreads();
+  hist[(int64_t)tid * nblocks + blockIdx.x] = h[tid];
+}
+
+__global__ __launch_bounds__(256) void k_radix_scatter(const int32_t* key_in, const int32_t* val_in, int64_t n,
+                                                       int shift, const int32_t* hist_scan, int nblocks,
+                                                       int32_t* key_out, int32_t* val_out) {
+  __shared__ int cnt[4][256];
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  for (int e = tid; e < 1024; e += 256) cnt[e >> 8][e & 255] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+  const bool valid = i < n;
+  int key = 0, val = 0, d = 0;
+  if (valid) {
+    key = key_in[i];
+    val = val_in[i];
+    d = (key >> shift) & 255;
+  }
+  uint64_t eq = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t m = __ballot((d >> bit) & 1);
+    eq &= ((d >> bit) & 1) ? m : ~m;
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  const int rank_w = __popcll(eq & lt);
+  const bool leader = valid && ((eq >> lane) == 1ull);
+  if (leader) cnt[wv][d] = __popcll(eq);
+  __syncthreads();
+  if (valid) {
+    int r = rank_w;
+    for (int w = 0; w < wv; ++w) r += cnt[w][d];
+    const int dst = hist_scan[(int64_t)d * nblocks + blockIdx.x] + r;
+    if (key_out) key_out[dst] = key;
+    val_out[dst] = val;
+  }
+}
+
+// ------------------------------------------------------------- transpose --
+__device__ __forceinline__ void row_coords(const IndexPtrs& ip, int r, int TQB, int& hs, int& b, int& qb) {
+  hs = r / TQB;
+  const int qg = r - hs * TQB;
+  b = ip.qb_seq[qg];
+  qb = qg - ip.qbase[b];
+}
+
+__global__ __launch_bounds__(256) void k_col_count(IndexPtrs ip, int64_t rbar) {
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB], TKB = ip.hdr[H_TKB];
+  if (r >= R || r >= rbar) return;
+  int hs, b, qb;
+  row_coords(ip, (int)r, TQB, hs, b, qb);
+  const int base = hs * TKB + ip.kbase[b];
+  for (int e = ip.row_ptr[r] + lane; e < ip.row_ptr[r + 1]; e += 64) atomicAdd(&ip.col_cnt[base + ip.cols[e]], 1);
+}
+
+__global__ __launch_bounds__(256) void k_col_fill(IndexPtrs ip, int64_t rbar) {
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB], TKB = ip.hdr[H_TKB];
+  if (r >= R || r >= rbar) return;
+  int hs, b, qb;
+  row_coords(ip, (int)r, TQB, hs, b, qb);
+  const int base = hs * TKB + ip.kbase[b];
+  for (int e = ip.row_ptr[r] + lane; e < ip.row_ptr[r + 1]; e += 64) {
+    const int c = base + ip.cols[e];
+    const int slot = atomicAdd(&ip.col_fill[c], 1);
+    ip.qrows[ip.col_ptr[c] + slot] = qb;
+  }
+}
+
+// Puts each column's q-block list in ascending order (one wave per column).
+__global__ __launch_bounds__(256) void k_col_sort(IndexPtrs ip, int64_t cbar, int words, int bx) {
+  extern __shared__ uint32_t smem_bm[];
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  uint32_t* bm = smem_bm + wv * words;
+  const int64_t c = (int64_t)blockIdx.x * 4 + wv;
+  const int C = ip.hdr[H_C], TKB = ip.hdr[H_TKB];
+  int nqb = 0, p0 = 0, p1 = 0;
+  if (c < C && c < cbar) {
+    const int kg = (int)(c % TKB);
+    const int b = ip.kb_seq[kg];
+    nqb = cdiv(ip.sq[b], bx);
+    p0 = ip.col_ptr[c];
+    p1 = ip.col_ptr[c + 1];
+  }
+  const int nwords = (nqb + 31) >> 5;
+  for (int w = lane; w < nwords; w += 64) bm[w] = 0;
+  __syncthreads();
+  for (int e = p0 + lane; e < p1; e += 64) {
+    const int qb = ip.qrows[e];
+    atomicOr(&bm[qb >> 5], 1u << (qb & 31));
+  }
+  __syncthreads();
+  int pos = p0;
+  for (int cc = 0; cc < nwords; cc += 64) {
+    const int w = cc + lane;
+    uint32_t word = w < nwords ? bm[w] : 0u;
+    const int pc = __popc(word);
+    const int inc = wave_incl_scan(pc);
+    int o = pos + inc - pc;
+    while (word) {
+      const int bit = __ffs(word) - 1;
+      ip.qrows[o++] = w * 32 + bit;
+      word &= word - 1;
+    }
+    pos += __shfl(inc, 63, 64);
+  }
+}
+
+// Sort keys of the dK/dV items: item i = g * TKB + kg, load = number of
+// (sparse head of group g, q-block) pairs that reach KV block kg.
+__global__ __launch_bounds__(256) void k_kv_keys(IndexPtrs ip, int64_t kvbar, int hs_total, int n2, int group,
+                                                 int kvkey_max) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= kvbar) return;
+  const int TKB = ip.hdr[H_TKB];
+  const int items = n2 * TKB;
+  int key = kvkey_max + 1;
+  if (i < items) {
+    const int g = (int)(i / TKB), kg = (int)(i % TKB);
+    int load = 0;
+    if (hs_total == n2) {
+      load = ip.col_cnt[g * TKB + kg];
+    } else {
+      for (int h = g * group; h < (g + 1) * group; ++h) load += ip.col_cnt[h * TKB + kg];
+    }
+    key = kvkey_max - load;
+  }
+  ip.key0[i] = key;
+  ip.val0[i] = (int)i;
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* p, int64_t n, int v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+int radix_passes(int64_t maxkey) {
+  int bits = 0;
+  while ((maxkey >> bits) != 0) ++bits;
+  return bits <= 8 ? 1 : (bits + 7) / 8;
+}
+
+// Sorts (key0, val0)[0..n) and writes the values in key order to `dst`.
+hipError_t radix_sort(const IndexPtrs& ip, int64_t n, int64_t maxkey, int32_t* dst, hipStream_t st) {
+  const int nb = (int)blocks_for(n, 256);
+  const int passes = radix_passes(maxkey);
+  int32_t *ki = ip.key0, *vi = ip.val0, *ko = ip.key1, *vo = ip.val1;
+  for (int p = 0; p < passes; ++p) {
+    const bool last = p == passes - 1;
+    k_radix_hist<<<nb, 256, 0, st>>>(ki, n, 8 * p, ip.hist, nb);
+    k_scan_excl<<<1, 1024, 0, st>>>(ip.hist, ip.hist, (int64_t)nb * 256, nullptr);
+    k_radix_scatter<<<nb, 256, 0, st>>>(ki, vi, n, 8 * p, ip.hist, nb, last ? nullptr : ko, last ? dst : vo);
+    int32_t* t = ki; ki = ko; ko = t;
+    t = vi; vi = vo; vo = t;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip, int n2,
+                        int group, bool with_csc, hipStream_t st) {
+  k_setup<<<1, 256, 0, st>>>(seq, ip, sel.hs, n2);
+  const int words = (bd.nkb_max + 31) / 32 > 0 ? (bd.nkb_max + 31) / 32 : 1;
+  const size_t lds = 4 * (size_t)words * 4;
+  const unsigned rgrid = blocks_for(bd.rbar, 4);
+  k_row_count<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words, bd.cmax);
+  k_scan_excl<<<1, 1024, 0, st>>>(ip.row_cnt, ip.row_ptr, bd.rbar, ip.hdr + H_NNZ);
+  k_row_fill<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words);
+  hipError_t e = radix_sort(ip, bd.rbar, (int64_t)bd.cmax + 1, ip.work, st);
+  if (e != hipSuccess || !with_csc) return e;
+  k_fill_i32<<<blocks_for(bd.cbar, 256), 256, 0, st>>>(ip.col_cnt, bd.cbar, 0);
+  k_fill_i32<<<blocks_for(bd.cbar, 256), 256, 0, st>>>(ip.col_fill, bd.cbar, 0);
+  k_col_count<<<rgrid, 256, 0, st>>>(ip, bd.rbar);
+  k_scan_excl<<<1, 1024, 0, st>>>(ip.col_cnt, ip.col_ptr, bd.cbar, nullptr);
+  k_col_fill<<<rgrid, 256, 0, st>>>(ip, bd.rbar);
+  const int qwords = (bd.nqb_max + 31) / 32 > 0 ? (bd.nqb_max + 31) / 32 : 1;
+  k_col_sort<<<blocks_for(bd.cbar, 4), 256, 4 * (size_t)qwords * 4, st>>>(ip, bd.cbar, qwords, seq.bx);
+  k_kv_keys<<<blocks_for(bd.kvbar, 256), 256, 0, st>>>(ip, bd.kvbar, sel.hs, n2, group, bd.kvkey_max);
+  return radix_sort(ip, bd.kvbar, (int64_t)bd.kvkey_max + 1, ip.work_kv, st);
+}
+
+}  // namespace bsa

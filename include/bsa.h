@@ -1,0 +1,220 @@
+/*
+ * bsa.h -- variable-length (TND-packed) block-sparse FlashAttention for
+ * AMD Instinct MI355X (gfx950), C ABI of libbsa.so.
+ *
+ * The operation.  For every sequence b, q-head h and query row i the forward
+ * pass computes softmax(scale * q_i K_sel^T) V_sel over the keys j that row i
+ * may attend to, and the natural-log log-sum-exp of the scaled scores
+ * (BlockSparseAttentionGrad README, "Function description", forward formula;
+ * GenericBlockSparseAttention page, "Sparse attention mechanism";
+ * BlitzSparseAttention page, "softmax_lse output").  The backward pass
+ * returns dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO with
+ * dS = P o (dO V^T - rowsum(dO o O)) (BlockSparseAttentionGrad README,
+ * backward formulas).
+ *
+ * Key j (local to sequence b) is allowed for query i (local) when
+ *   (a) block floor(j / block_y) is selected for q-block floor(i / block_x)
+ *       of sparse head hs(h) (see BSA_SPARSE_*),
+ *   (b) j < Skv_b, and
+ *   (c) with BSA_MASK_CAUSAL, j <= i + Skv_b - Sq_b (causal mask aligned at
+ *       the bottom-right corner, the FlashAttention UnpaddingScoreGradV2
+ *       page's rightDownCausal, the only causal mode of its TND layout).
+ * A row with no allowed key gets O = 0 and lse = +inf; in the backward pass
+ * its dQ is 0, and keys no row reaches get dK = dV = 0.
+ *
+ * A selection is a set: duplicate entries count once, entry order does not
+ * matter, entries outside [0, nKB_b) are skipped, an idx count is clamped to
+ * [0, W], and rows past the selection tensor's row dimension select nothing.
+ * KV block indices are local to their sequence.  q-head h reads KV head
+ * h / (N1 / N2).
+ *
+ * Two-stage use, following the pages' two-stage calls (size query, then
+ * execute on a stream; GenericBlockSparseAttention page, "aclnn API"):
+ *   1. bsa_get_workspace_size(): host only, checks the descriptor and returns
+ *      the device workspace each call needs.
+ *   2. bsa_fwd() / bsa_bwd(): enqueue all work on `stream` and return.  Each
+ *      call rebuilds its block index in the workspace first (the pages
+ *      require the schedule metadata to be regenerated for every call).
+ *
+ * Ownership.  Every pointer argument of stage 2 is caller-owned device
+ * memory (except the descriptor, a host pointer).  The library never
+ * allocates, frees or synchronizes; outputs are fully overwritten (no
+ * pre-zeroing needed) and must not alias inputs or the workspace; workspace
+ * contents are undefined on entry and exit.  Calls on different streams with
+ * different workspaces may run concurrently.
+ *
+ * Errors.  Status codes reuse the pages' numbers (GenericBlockSparseAttention
+ * page, first-stage return codes).  Device-resident values (cu_seqlens,
+ * seqused_kv, block_table entries) are not validated, as on the pages
+ * (GenericBlockSparseAttention page, "values are not checked at tiling
+ * time"): inconsistent values are undefined behaviour, except out-of-range
+ * *selection* entries, which are defined as skipped.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_PARAM_NULLPTR = 161001, /* a required pointer is NULL */
+  BSA_ERR_PARAM_INVALID = 161002, /* unsupported dtype/shape/attribute, or workspace too small */
+  BSA_ERR_INNER = 561103,         /* a valid combination with no compiled kernel variant */
+  BSA_ERR_RUNTIME = 561000        /* a HIP launch or runtime error */
+} bsa_status_t;
+
+enum { BSA_DTYPE_F16 = 1, BSA_DTYPE_BF16 = 2 };
+
+/* How the per-q-block KV block selection is given (argument `sparse`). */
+enum {
+  /* every KV block of the sequence is selected; `sparse` is ignored */
+  BSA_SPARSE_NONE = 0,
+  /* uint8 [B, Hs, sparse_rows, sparse_width], nonzero = compute column kb
+     (BlockSparseAttentionGrad README, blockSparseMaskOptional) */
+  BSA_SPARSE_BLOCK_MASK = 1,
+  /* uint16 [B, Hs, sparse_rows, sparse_width], KV block indices, 0xFFFF =
+     unused slot (BlitzSparseAttention page, sabi section) */
+  BSA_SPARSE_SABI_U16 = 2,
+  /* int32 [Hs, sparse_rows, sparse_width] over global q-blocks (sparse_rows =
+     totalQBlocks = sum_b ceil(Sq_b / block_x)), -1 = unused, plus
+     `sparse_count` int32 [Hs, sparse_rows]: the first count entries are live
+     (GenericBlockSparseAttention page, sparseBlockIdx / sparseBlockCount) */
+  BSA_SPARSE_IDX_I32 = 3
+};
+
+enum { BSA_MASK_NONE = 0, BSA_MASK_CAUSAL = 1 };
+
+/* K/V layout: packed [T_kv, N2, D] rows addressed through cu_seqlens_kv, or
+   paged [pages, page_size, N2, D] through block_table + seqused_kv
+   (GenericBlockSparseAttention page, "Paged Attention", PA_BBND). */
+enum { BSA_KV_TND = 0, BSA_KV_PAGED = 1 };
+
+typedef struct bsa_problem {
+  uint32_t struct_size;      /* sizeof(bsa_problem_t) */
+  int32_t dtype;             /* BSA_DTYPE_*: q, k, v, out, dout, dq, dk, dv */
+  int32_t batch;             /* B >= 0 */
+  int32_t num_heads_q;       /* N1 in [1, 256] */
+  int32_t num_heads_kv;      /* N2 >= 1, N1 % N2 == 0, N1 / N2 <= 128 */
+  int32_t head_dim;          /* D in {64, 128} */
+  int64_t total_q;           /* T_q: rows of q/out/dout/dq (= cu_seqlens_q[B]) */
+  int64_t total_kv;          /* T_kv rows of k/v (TND) or number of pages (paged) */
+  int32_t max_seqlen_q;      /* upper bound on every Sq_b */
+  int32_t max_seqlen_kv;     /* upper bound on every Skv_b */
+  int32_t block_x;           /* q rows per selection block; 128 */
+  int32_t block_y;           /* keys per selection block; multiple of 64, <= 4096 */
+  int32_t sparse_kind;       /* BSA_SPARSE_* */
+  int32_t sparse_heads;      /* Hs: N1 (pattern per q-head) or N2 (shared by a GQA group) */
+  int32_t sparse_rows;       /* row dimension of the selection tensor (see BSA_SPARSE_*) */
+  int32_t sparse_width;      /* W: columns (mask), slots (sabi) or topK (idx, <= 256) */
+  int32_t mask_type;         /* BSA_MASK_* */
+  int32_t kv_layout;         /* BSA_KV_* */
+  int32_t page_size;         /* paged: tokens per page, multiple of 64 */
+  int32_t max_pages_per_seq; /* paged: second dimension of block_table */
+  int64_t page_stride;       /* paged: elements between pages, >= page_size*N2*D, multiple of N2*D */
+  double scale;              /* > 0, or 0 for 1/sqrt(D); applied rounded to fp32 */
+  uint32_t flags;            /* reserved, must be 0 */
+  uint32_t reserved;         /* must be 0 */
+} bsa_problem_t;
+
+/* Stage 1.  Checks `p` and writes the workspace bytes bsa_fwd (`fwd_bytes`)
+ * and bsa_bwd (`bwd_bytes`) need; either out-pointer may be NULL, not both.
+ * Host only, no device work.  Sizes come from host-known bounds (total_q,
+ * total_kv, maximum lengths, selection shape), never from device values.
+ * Returns BSA_ERR_PARAM_NULLPTR, BSA_ERR_PARAM_INVALID for an unsupported
+ * descriptor, BSA_ERR_INNER for a valid one with no compiled variant. */
+bsa_status_t bsa_get_workspace_size(const bsa_problem_t* p, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* Stage 2, forward.
+ *   q            [T_q, N1, D]           dtype, contiguous
+ *   k, v         [T_kv, N2, D] (TND) or [pages, page_size, N2, D] (paged,
+ *                page axis strided by page_stride elements)
+ *   cu_seqlens_q int64 [B+1], cu_seqlens_q[0] = 0, non-decreasing
+ *   cu_seqlens_kv int64 [B+1] (TND; NULL when paged)
+ *   seqused_kv   int32 [B] (paged: required; TND: NULL)
+ *   sparse       selection tensor per p->sparse_kind (NULL for NONE)
+ *   sparse_count int32 [Hs, sparse_rows] (IDX only, else NULL)
+ *   block_table  int32 [B, max_pages_per_seq] (paged only, else NULL); only
+ *                entries for pages holding keys < Skv_b are read
+ *   out          [T_q, N1, D] dtype
+ *   lse          float32 [T_q, N1], natural log of the scaled scores' sum
+ * Returns BSA_ERR_PARAM_NULLPTR when a required pointer is NULL,
+ * BSA_ERR_PARAM_INVALID when workspace_bytes is below the stage-1 value,
+ * BSA_ERR_RUNTIME on a HIP error.  B == 0 or T_q == 0: BSA_OK, nothing done. */
+bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const void* v,
+                     const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                     const int32_t* seqused_kv, const void* sparse, const int32_t* sparse_count,
+                     const int32_t* block_table, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Stage 2, backward.  Inputs as bsa_fwd plus `out` and `lse` from the forward
+ * pass and `dout` [T_q, N1, D].  Outputs dq [T_q, N1, D], dk and dv with k's
+ * shape (TND only: the paged layout returns BSA_ERR_INNER from stage 1's
+ * bwd_bytes query and from this call).  dQ is computed by a separate
+ * Q-block-major pass, so results are deterministic run to run. */
+bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const void* v,
+                     const void* out, const void* dout, const float* lse,
+                     const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                     const int32_t* seqused_kv, const void* sparse, const int32_t* sparse_count,
+                     const int32_t* block_table, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* The block index the passes build (the role of GenericBlockSparseAttention's
+ * metadata pre-operator: a load-balanced schedule computed before the main
+ * kernel).  bsa_build_index enqueues only the index construction into the
+ * workspace; bsa_index_view says where each product sits.  Layout (all int32,
+ * see the field comments):
+ *   header[0..7]: totalQBlocks, totalKBlocks, R = Hs*totalQBlocks rows,
+ *                 C = Hs*totalKBlocks columns, nnz, N2*totalKBlocks kv items, 0, 0
+ *   row_ptr[R+1], cols[nnz]: per row r = hs*totalQBlocks + qbase_b + qb the
+ *                 ascending local KV blocks holding at least one allowed pair
+ *   work[R]:      rows by visited count descending, ties by row id
+ *   with_csc != 0 adds
+ *   col_ptr[C+1], qrows[nnz]: per column c = hs*totalKBlocks + kbase_b + kb the
+ *                 ascending local q-blocks that visit it
+ *   work_kv[N2*totalKBlocks]: items g*totalKBlocks + kbase_b + kb by the number
+ *                 of (sparse head of group g, q-block) pairs reaching them,
+ *                 descending, ties by item id.
+ * The workspace needed is at most bsa_get_workspace_size's fwd_bytes
+ * (with_csc == 0) or bwd_bytes (with_csc != 0). */
+typedef struct bsa_index_view {
+  uint64_t off_header, off_row_ptr, off_cols, off_work, off_col_ptr, off_qrows, off_work_kv;
+  int64_t max_rows, max_cols, max_nnz, max_kv_items;
+} bsa_index_view_t;
+
+bsa_status_t bsa_index_view(const bsa_problem_t* p, int with_csc, bsa_index_view_t* view);
+
+bsa_status_t bsa_build_index(const bsa_problem_t* p, const int64_t* cu_seqlens_q,
+                             const int64_t* cu_seqlens_kv, const int32_t* seqused_kv,
+                             const void* sparse, const int32_t* sparse_count, int with_csc,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static string naming `s`. */
+const char* bsa_status_string(bsa_status_t s);
+
+/* Per-kernel timing with HIP events recorded on the launch stream, for
+ * measurement tools.  While enabled (nonzero) every launch of the library's
+ * kernels is bracketed by events; bsa_profile_read() synchronizes on the
+ * recorded events and returns, for kernel id `kernel` (BSA_KERNEL_*), the
+ * number of launches and their summed duration in milliseconds since the last
+ * bsa_profile_reset().  Not for use while another thread calls the library. */
+enum {
+  BSA_KERNEL_INDEX = 0, /* all block-index kernels together */
+  BSA_KERNEL_FWD = 1,
+  BSA_KERNEL_BWD_PRE = 2,
+  BSA_KERNEL_BWD_DKDV = 3,
+  BSA_KERNEL_BWD_DQ = 4,
+  BSA_KERNEL_COUNT = 5
+};
+bsa_status_t bsa_profile_enable(int enable);
+bsa_status_t bsa_profile_reset(void);
+bsa_status_t bsa_profile_read(int kernel, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H_ */

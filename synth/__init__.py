@@ -141,8 +141,27 @@ def _cdiv(a, b):
     return -(-int(a) // int(b))
 
 
-def _values(rng, shape, dtype):
-    return round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+_CHUNK = 1 << 22  # elements per draw; keeps temporaries small and reused
+
+
+def _values(rng, shape, dtype, nan_mask=None):
+    """N(0, 1) float32 draws of ``shape`` rounded to ``dtype``, generated in
+    chunks along axis 0 (the generator's stream is the same as one draw).
+    ``nan_mask`` (boolean over the leading axes) marks rows set to NaN."""
+    shape = tuple(int(x) for x in shape)
+    bits = np.empty(shape, dtype=np.uint16)
+    vals = np.empty(shape, dtype=np.float32)
+    if bits.size == 0:
+        return bits, vals
+    row = int(np.prod(shape[1:]))
+    step = max(1, _CHUNK // max(row, 1))
+    for a in range(0, shape[0], step):
+        b = min(shape[0], a + step)
+        x = rng.standard_normal((b - a,) + shape[1:], dtype=np.float32)
+        if nan_mask is not None:
+            x[nan_mask[a:b]] = np.nan
+        bits[a:b], vals[a:b] = round_to_dtype(x, dtype)
+    return bits, vals
 
 
 def _finish(rng, c: dict, with_dout: bool, kv_shape, nan_tail_mask=None, values=True):
@@ -154,13 +173,8 @@ def _finish(rng, c: dict, with_dout: bool, kv_shape, nan_tail_mask=None, values=
         return Case(**c)
     dt = c["dtype"]
     c["q_bits"], c["q"] = _values(rng, (T, N1, D), dt)
-    kf = rng.standard_normal(kv_shape, dtype=np.float32)
-    vf = rng.standard_normal(kv_shape, dtype=np.float32)
-    if nan_tail_mask is not None:
-        kf[nan_tail_mask] = np.nan
-        vf[nan_tail_mask] = np.nan
-    c["k_bits"], c["k"] = round_to_dtype(kf, dt)
-    c["v_bits"], c["v"] = round_to_dtype(vf, dt)
+    c["k_bits"], c["k"] = _values(rng, kv_shape, dt, nan_tail_mask)
+    c["v_bits"], c["v"] = _values(rng, kv_shape, dt, nan_tail_mask)
     if with_dout:
         c["dout_bits"], c["dout"] = _values(rng, (T, N1, D), dt)
     return Case(**c)

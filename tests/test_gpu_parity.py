@@ -1,0 +1,294 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Index products must be bit-exact; floating point must meet the tolerances
+fixed for the method: max-abs error on O <= 1e-2 (bf16) / 5e-3 (fp16), lse
+within 1e-3 (+inf exactly where the oracle has +inf), relative Frobenius error
+on dQ/dK/dV <= 2e-2 (bf16) / 1e-2 (fp16).
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from block_sparse_varlen_amd.runner import DeviceCase
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"bf16": 1e-2, "f16": 5e-3}
+TOL_G = {"bf16": 2e-2, "f16": 1e-2}
+TOL_LSE = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------- cases --
+
+def fwd_cases():
+    R = synth.random_case
+    return {
+        "mask_f16_d64_ragged_empty_seq": R(101, lens_q=[300, 0, 517], N1=2, D=64, dtype="f16", kind="mask"),
+        "mask_gqa_shared_causal": R(102, lens_q=[200, 385], N1=4, N2=2, D=128, kind="mask", sparse_heads=2,
+                                    causal=True, density=0.6),
+        "sabi_messy_causal_by256": R(103, lens_q=[257, 130], lens_kv=[600, 70], N1=2, D=128, kind="sabi",
+                                     by=256, causal=True, messy=True),
+        "idx_messy_gqa4_by64": R(104, lens_q=[300, 450], lens_kv=[200, 640], N1=4, N2=1, D=128, kind="idx",
+                                 sparse_heads=1, by=64, messy=True, width=6),
+        "idx_paged_causal": R(105, lens_q=[500, 310], lens_kv=[400, 700], N1=4, N2=2, D=128, kind="idx",
+                              sparse_heads=2, causal=True, paged=True),
+        "none_causal": R(106, lens_q=[129, 384, 1], N1=2, D=128, kind="none", causal=True),
+        "none_long_kv_by512_f16": R(107, lens_q=[100], lens_kv=[1000], N1=2, D=128, dtype="f16", kind="none",
+                                    by=512),
+        "sabi_perhead_gqa_paged": R(108, lens_q=[260, 333], N1=4, N2=2, D=128, kind="sabi", sparse_heads=4,
+                                    paged=True),
+        "mask_d64_bf16_causal_qlong": R(109, lens_q=[700], lens_kv=[260], N1=2, D=64, kind="mask",
+                                        causal=True, density=0.7),
+    }
+
+
+def bwd_cases():
+    R = synth.random_case
+    return {
+        "mask_f16_d64_ragged_empty_seq": R(201, lens_q=[300, 0, 517], N1=2, D=64, dtype="f16", kind="mask"),
+        "mask_gqa_shared_causal": R(202, lens_q=[200, 385], N1=4, N2=2, D=128, kind="mask", sparse_heads=2,
+                                    causal=True, density=0.6),
+        "sabi_messy_causal_by256": R(203, lens_q=[257, 130], lens_kv=[600, 70], N1=2, D=128, kind="sabi",
+                                     by=256, causal=True, messy=True),
+        "idx_perhead_gqa": R(204, lens_q=[300, 450], lens_kv=[200, 640], N1=4, N2=2, D=128, kind="idx",
+                             sparse_heads=4, width=5),
+        "none_causal_f16": R(205, lens_q=[129, 384, 1], N1=2, D=128, dtype="f16", kind="none", causal=True),
+        "none_sq_lt_skv": R(206, lens_q=[100], lens_kv=[1000], N1=2, D=128, kind="none", causal=True),
+    }
+
+
+FWD = fwd_cases()
+BWD = bwd_cases()
+
+
+def empty_rows_case():
+    c = synth.random_case(110, lens_q=[384], N1=2, D=128, kind="mask")
+    c.sparse[:, :, 1, :] = 0  # q-block 1 selects nothing -> O = 0, lse = +inf
+    c.sparse[:, 1, :, 2] = 0  # kv block 2 unreached by head 1 -> dK = dV = 0 there
+    return c
+
+
+# ----------------------------------------------------------------- helpers --
+
+def check_fwd(case, dc, sample=None, tag=""):
+    O = dc.out.float().cpu().numpy()
+    L = dc.lse.cpu().numpy()
+    Or, Lr = oracle.forward(case, sample)
+    sel = ~np.isnan(Lr)
+    if sample is None:
+        assert sel.all()
+    err = np.abs(O[sel] - Or[sel]).max() if sel.any() else 0.0
+    inf_r = np.isinf(Lr) & sel
+    assert np.array_equal(np.isinf(L) & sel, inf_r), f"{tag}: +inf lse positions differ"
+    fin = sel & ~inf_r
+    lerr = np.abs(L[fin] - Lr[fin]).max() if fin.any() else 0.0
+    say(f"  {tag}: max|dO|={err:.3e} max|dlse|={lerr:.3e} rows={int(sel.sum())}")
+    assert err <= TOL_O[case.dtype], f"{tag}: O error {err}"
+    assert lerr <= TOL_LSE, f"{tag}: lse error {lerr}"
+
+
+def rel_fro(x, r):
+    d = np.linalg.norm((x - r).ravel())
+    n = np.linalg.norm(r.ravel())
+    return d / n if n > 0 else d
+
+
+def check_bwd(case, dc, tag=""):
+    dq = dc.dq.float().cpu().numpy()
+    dk = dc.dk.float().cpu().numpy()
+    dv = dc.dv.float().cpu().numpy()
+    rq, rk, rv = oracle.backward(case)
+    eq, ek, ev = rel_fro(dq, rq), rel_fro(dk, rk), rel_fro(dv, rv)
+    say(f"  {tag}: rel_fro dq={eq:.3e} dk={ek:.3e} dv={ev:.3e}")
+    tol = TOL_G[case.dtype]
+    assert eq <= tol and ek <= tol and ev <= tol
+    # structural zeros: q rows with no allowed key (lse = +inf) get dq = 0;
+    # keys no row reaches (dv row exactly 0 in the oracle) get dk = dv = 0
+    _, lse_r = oracle.forward(case)
+    assert np.all(dq[np.isinf(lse_r)] == 0)
+    unreached = np.all(rv == 0, axis=-1)
+    assert np.all(dk[unreached] == 0) and np.all(dv[unreached] == 0)
+
+
+def nan_fill(*ts):
+    for t in ts:
+        t.fill_(float("nan"))
+
+
+# ------------------------------------------------------------------- index --
+
+@pytest.mark.parametrize("name", list(FWD))
+def test_index_bit_exact(name):
+    case = FWD[name]
+    say(f"index {name}")
+    with_csc = not case.paged and case.by % 128 == 0  # backward variants need 128-key tiles
+    dc = DeviceCase(case, with_bwd=with_csc)
+    got = dc.index(with_csc)
+    ref = oracle.index_products(case, with_csc=with_csc)
+    assert got["R"] == ref["R"]
+    for k in ("row_ptr", "cols", "work"):
+        assert np.array_equal(got[k], ref[k]), k
+    if with_csc:
+        for k in ("col_ptr", "qrows", "work_kv"):
+            assert np.array_equal(got[k], ref[k]), k
+
+
+# --------------------------------------------------------------------- fwd --
+
+@pytest.mark.parametrize("name", list(FWD) + ["empty_rows"])
+def test_fwd_small(name):
+    case = FWD[name] if name != "empty_rows" else empty_rows_case()
+    say(f"fwd {name}")
+    dc = DeviceCase(case, with_bwd=False)
+    nan_fill(dc.out, dc.lse)
+    dc.fwd()
+    torch.cuda.synchronize()
+    check_fwd(case, dc, tag=name)
+
+
+def test_fwd_deterministic():
+    case = FWD["idx_paged_causal"]
+    dc = DeviceCase(case, with_bwd=False)
+    dc.fwd()
+    o1, l1 = dc.out.clone(), dc.lse.clone()
+    dc.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), dc.out.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), dc.lse.view(torch.int32))
+
+
+# --------------------------------------------------------------------- bwd --
+
+@pytest.mark.parametrize("name", list(BWD) + ["empty_rows"])
+def test_bwd_small(name):
+    case = BWD[name] if name != "empty_rows" else empty_rows_case()
+    say(f"bwd {name}")
+    dc = DeviceCase(case, with_bwd=True)
+    dc.fwd()
+    nan_fill(dc.dq, dc.dk, dc.dv)
+    dc.bwd()
+    torch.cuda.synchronize()
+    check_bwd(case, dc, tag=name)
+
+
+def test_bwd_deterministic():
+    case = BWD["mask_gqa_shared_causal"]
+    dc = DeviceCase(case, with_bwd=True)
+    dc.fwd()
+    dc.bwd()
+    g1 = [t.clone() for t in (dc.dq, dc.dk, dc.dv)]
+    dc.bwd()
+    torch.cuda.synchronize()
+    for a, b in zip(g1, (dc.dq, dc.dk, dc.dv)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------- benchmark workloads --
+
+@functools.lru_cache(maxsize=1)
+def _cfg(n):
+    return synth.CONFIGS[n]()
+
+
+def _sample_rows(case, idx, n_rand, seed):
+    """Longest rows first, then random (b, h, qb) triples, then the last
+    q-block of every sequence."""
+    G = case.N1 // case.N2
+    rng = np.random.default_rng(seed)
+    TQB = idx["TQB"]
+    qbase = np.concatenate([[0], np.cumsum([-(-int(s) // case.bx) for s in np.diff(case.cu_q)])])
+    out = set()
+
+    def add_row(r):
+        hs, qg = divmod(int(r), TQB)
+        b = int(np.searchsorted(qbase, qg, side="right") - 1)
+        qb = qg - int(qbase[b])
+        heads = [hs] if case.sparse_heads == case.N1 else list(range(hs * G, (hs + 1) * G))
+        for h in heads[:2]:
+            out.add((b, h, qb))
+
+    for r in idx["work"][:4]:
+        add_row(r)
+    for r in rng.choice(idx["R"], size=min(n_rand, idx["R"]), replace=False):
+        add_row(r)
+    for b in range(case.B):
+        n = -(-int(case.cu_q[b + 1] - case.cu_q[b]) // case.bx)
+        if n:
+            out.add((b, int(rng.integers(case.N1)), n - 1))
+    return sorted(out)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_fwd_config(n):
+    say(f"config {n}: generating")
+    case = _cfg(n)
+    say(f"config {n}: fwd on GPU")
+    dc = DeviceCase(case, with_bwd=False)
+    nan_fill(dc.out, dc.lse)
+    dc.fwd()
+    torch.cuda.synchronize()
+    assert not torch.isnan(dc.out).any() and not torch.isnan(dc.lse).any()
+    idx = oracle.index_products(case, with_csc=False)
+    got = dc.index(False)
+    for k in ("row_ptr", "cols", "work"):
+        assert np.array_equal(got[k], idx[k]), k
+    sample = None if n == 1 else _sample_rows(case, idx, 24, n)
+    check_fwd(case, dc, sample=sample, tag=f"config{n}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n", [1, 2, 5])
+def test_bwd_config(n):
+    case = _cfg(n)
+    say(f"config {n}: bwd on GPU")
+    dc = DeviceCase(case, with_bwd=True)
+    dc.fwd()
+    nan_fill(dc.dq, dc.dk, dc.dv)
+    dc.bwd()
+    torch.cuda.synchronize()
+    for t in (dc.dq, dc.dk, dc.dv):
+        assert not torch.isnan(t).any()
+    got = dc.index(True)
+    idx = oracle.index_products(case, with_csc=True)
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+        assert np.array_equal(got[k], idx[k]), k
+    if n == 1:
+        check_bwd(case, dc, tag="config1")
+        return
+    rng = np.random.default_rng(100 + n)
+    rows = _sample_rows(case, idx, 12, 50 + n)
+    kbase = np.concatenate([[0], np.cumsum([-(-int(s) // case.by) for s in np.diff(case.cu_kv)])])
+    kvs = set()
+    for it in list(idx["work_kv"][:3]) + list(rng.choice(len(idx["work_kv"]), 6, replace=False)):
+        g, kg = divmod(int(it), idx["TKB"])
+        b = int(np.searchsorted(kbase, kg, side="right") - 1)
+        kvs.add((b, g, kg - int(kbase[b])))
+    rq, rk, rv = oracle.backward(case, sample_rows=rows, sample_kv=sorted(kvs))
+    dq = dc.dq.float().cpu().numpy()
+    dk = dc.dk.float().cpu().numpy()
+    dv = dc.dv.float().cpu().numpy()
+    selq = ~np.isnan(rq[..., 0])
+    tol = TOL_G[case.dtype]
+    eq = rel_fro(dq[selq], rq[selq])
+    keys = []
+    for (b, g, kb) in kvs:
+        k0 = int(case.cu_kv[b]) + kb * case.by
+        k1 = min(int(case.cu_kv[b + 1]), k0 + case.by)
+        keys += [(j, g) for j in range(k0, k1)]
+    kj = np.array([x[0] for x in keys])
+    kgs = np.array([x[1] for x in keys])
+    ek = rel_fro(dk[kj, kgs], rk[kj, kgs])
+    ev = rel_fro(dv[kj, kgs], rv[kj, kgs])
+    say(f"  config{n}: rel_fro dq={eq:.3e} dk={ek:.3e} dv={ev:.3e} (sampled)")
+    assert eq <= tol and ek <= tol and ev <= tol
