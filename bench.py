@@ -1,0 +1,240 @@
+"""Throughput of block-sparse varlen attention (forward + backward) on one
+MI355X.
+
+Workload: the long-context block-sparse case -- 2 sequences x 16384 tokens,
+16 q/kv heads, D = 128, bf16, 128x128 blocks, a block-causal mask keeping the
+diagonal, the 4 preceding and 8 random earlier blocks per q-block.  One step
+= one bsa_fwd + one bsa_bwd call (each rebuilding its block index), inputs
+resident in HBM.  FLOPs are counted over the selected blocks only: 4 r c D
+per visited (q-head, q-block, kv-block) pair forward and 10 r c D backward
+(r, c = valid rows / columns of the pair).
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+METRIC = "fwd & bwd TFLOP/s over selected blocks; % of MI355X bf16 MFMA peak"
+WORKLOAD = "long-context block-sparse fwd+bwd: TND 2x16384, N1=N2=16, D=128, bf16, 128x128 blocks, " \
+           "block-causal mask (diagonal + 4 preceding + 8 random earlier blocks per q-block)"
+# GEMMs each kernel performs out of the counted ones: fwd = QK^T, PV (4 r c D);
+# dK/dV kernel = S, dP, dV, dK (8 r c D); dQ kernel = dQ (2 r c D; its
+# recomputation of S and dP is not counted).
+ALG_FLOPS_PER_RCD = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_cfg5.json")
+KERNEL_SOURCES = {
+    "fwd": ["bsa_fwd.hip", "bsa_attn.h", "bsa_device.h", "bsa_internal.h"],
+    "bwd_dkdv": ["bsa_bwd.hip", "bsa_attn.h", "bsa_device.h", "bsa_internal.h"],
+    "bwd_dq": ["bsa_bwd.hip", "bsa_attn.h", "bsa_device.h", "bsa_internal.h"],
+}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "block_sparse_varlen_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def visited_rcd(case, idx):
+    """Sum over visited (q-head, q-block, kv-block) pairs of r * c * D."""
+    lens_q = np.diff(case.cu_q)
+    lens_kv = np.diff(case.cu_kv)
+    nqb = -(-lens_q // case.bx)
+    qbase = np.concatenate([[0], np.cumsum(nqb)])
+    TQB, R = idx["TQB"], idx["R"]
+    rp, cols = idx["row_ptr"], idx["cols"]
+    hpr = 1 if case.sparse_heads == case.N1 else case.N1 // case.N2
+    total = 0
+    for r in range(R):
+        qg = r % TQB
+        b = int(np.searchsorted(qbase, qg, side="right") - 1)
+        qb = qg - int(qbase[b])
+        rows = min(case.bx, int(lens_q[b]) - qb * case.bx)
+        kb = cols[rp[r]:rp[r + 1]].astype(np.int64)
+        c = np.minimum(case.by, int(lens_kv[b]) - kb * case.by)
+        total += rows * int(c.sum())
+    return total * hpr * case.D
+
+
+def cpu_baseline(case, budget_s: float):
+    """The CPU oracle (fwd + bwd of whole q-blocks) timed on a random sample of
+    q-blocks of the same workload until ``budget_s`` seconds have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    lens_q = np.diff(case.cu_q)
+    nqb = -(-lens_q // case.bx)
+    rng = np.random.default_rng(0)
+    idx = oracle.index_products(case, with_csc=False)
+    rp = idx["row_ptr"]
+    TQB = idx["TQB"]
+    qbase = np.concatenate([[0], np.cumsum(nqb)])
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = int(rng.integers(case.B))
+        h = int(rng.integers(case.N1))
+        qb = int(rng.integers(nqb[b]))
+        oracle.forward(case, sample=[(b, h, qb)])
+        oracle.backward(case, sample_rows=[(b, h, qb)])
+        r = h * TQB + int(qbase[b]) + qb
+        rows = min(case.bx, int(lens_q[b]) - qb * case.bx)
+        kbs = idx["cols"][rp[r]:rp[r + 1]]
+        c = np.minimum(case.by, int(np.diff(case.cu_kv)[b]) - kbs * case.by).sum()
+        flops += 14.0 * rows * c * case.D
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} random (sequence, q-head, q-block) units of the same workload, fwd+bwd each, "
+                      f"{dt:.1f} s of fp64 NumPy (BLAS threads={threads})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 512 MiB elementwise copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import block_sparse_varlen_amd as bsa
+    from block_sparse_varlen_amd.runner import DeviceCase
+
+    torch.cuda.set_device(0)
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    case = synth.config5()
+    dc = DeviceCase(case, with_bwd=True)
+    idx = dc.index(False)
+    rcd = visited_rcd(case, idx)
+    f_fwd, f_bwd = 4.0 * rcd, 10.0 * rcd
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dc.fwd()
+        dc.bwd()
+
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing (HIP events on the launch stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # split fwd / bwd
+    ef = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms = bwd_ms = 0.0
+    for _ in range(args.steps):
+        ef[0].record(stream)
+        dc.fwd()
+        ef[1].record(stream)
+        dc.bwd()
+        ef[2].record(stream)
+        torch.cuda.synchronize()
+        fwd_ms += ef[0].elapsed_time(ef[1])
+        bwd_ms += ef[1].elapsed_time(ef[2])
+    fwd_ms /= args.steps
+    bwd_ms /= args.steps
+
+    # per-kernel durations from events the library records around its launches
+    bsa.bsa_profile_enable(True)
+    bsa.bsa_profile_reset()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for kid, name in bsa.KERNEL_NAMES.items():
+        n, tot = bsa.bsa_profile_read(kid)
+        if n:
+            per_kernel[name] = {"launches": n, "avg_ms": tot / n}
+    bsa.bsa_profile_enable(False)
+    print("bench: per-kernel " + json.dumps(per_kernel), file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        x = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        del x, y
+
+    dominant = max((k for k in per_kernel if k in ALG_FLOPS_PER_RCD), key=lambda k: per_kernel[k]["avg_ms"])
+    alg = ALG_FLOPS_PER_RCD[dominant] * rcd
+    achieved = alg / (per_kernel[dominant]["avg_ms"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        ent = tr.get(dominant)
+        if ent and ent.get("source_sha") == kernel_source_sha(dominant):
+            traffic = ent.get("bytes_per_launch")
+
+    total_tflops = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(total_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, seeded block mask)",
+        "config": {"workload": WORKLOAD, "global_batch": case.B, "seq_len": int(np.diff(case.cu_q).max()),
+                   "heads": case.N1, "head_dim": case.D, "block_shape": [case.bx, case.by],
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
+                "frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": f_fwd},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
+                "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": f_bwd},
+        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per_kernel.items()},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
