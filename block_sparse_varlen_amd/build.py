@@ -26,6 +26,9 @@ FLAGS = [
     "-Wno-unused-result",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax math reads them directly instead of
+    # copying them out of accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

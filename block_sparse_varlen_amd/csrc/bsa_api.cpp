@@ -16,6 +16,8 @@ using namespace bsa;
 namespace {
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// grid sizes are padded to whole XCD rounds (see xcd_item in bsa_attn.h)
+int64_t xcd_grid(int64_t items) { return cdiv64(items, NUM_XCD * XCD_SEG) * (NUM_XCD * XCD_SEG); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- checks --
@@ -380,7 +382,7 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
   prof_begin(BSA_KERNEL_FWD, s);
-  e = launch_fwd(a, p->dtype, p->head_dim, b.rbar * a.heads_per_row, s);
+  e = launch_fwd(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row), s);
   prof_end(BSA_KERNEL_FWD, s);
   return from_hip(e);
 }
@@ -453,13 +455,13 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
   if (p->total_kv > 0) {
     prof_begin(BSA_KERNEL_BWD_DKDV, s);
-    e = launch_bwd_dkdv(a, p->dtype, p->head_dim, b.kvbar * a.sub_tiles, s);
+    e = launch_bwd_dkdv(a, p->dtype, p->head_dim, xcd_grid(b.kvbar * a.sub_tiles), s);
     prof_end(BSA_KERNEL_BWD_DKDV, s);
     if (e != hipSuccess) return BSA_ERR_RUNTIME;
   }
   if (p->total_q > 0) {
     prof_begin(BSA_KERNEL_BWD_DQ, s);
-    e = launch_bwd_dq(a, p->dtype, p->head_dim, b.rbar * a.heads_per_row, s);
+    e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row), s);
     prof_end(BSA_KERNEL_BWD_DQ, s);
   }
   return from_hip(e);

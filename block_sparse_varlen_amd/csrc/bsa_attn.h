@@ -11,6 +11,18 @@ namespace bsa {
 constexpr int KT = 64;   // keys per sub-tile of the Q-major kernels
 constexpr int QT = 128;  // query rows per Q-major work item (4 waves x 32)
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  xcd_item maps dispatch index `bid` to a work item so that every XCD
+// takes runs of XCD_SEG consecutive items from the longest-first order --
+// neighbouring q-blocks (or KV blocks) of one head, which share most of the
+// tiles they read -- while the order across XCDs stays longest-first at a
+// granularity of 8 * XCD_SEG items.  Grids are padded to a multiple of
+// 8 * XCD_SEG; items past the end exit.
+__device__ __forceinline__ int64_t xcd_item(int64_t bid) {
+  const int64_t x = bid % NUM_XCD, k = bid / NUM_XCD;
+  return (k / XCD_SEG) * (NUM_XCD * XCD_SEG) + x * XCD_SEG + (k % XCD_SEG);
+}
+
 // A Q-major work item: one q-block of one q-head.
 struct QItem {
   int r;        // CSR row
@@ -26,70 +38,150 @@ struct QItem {
 __device__ __forceinline__ bool decode_qitem(int64_t item, const int32_t* hdr, const int32_t* work,
                                              const int32_t* qb_seq, const int32_t* qbase, const SeqArgs& seq,
                                              int heads_per_row, int group, QItem& it) {
-  const int R = hdr[H_R];
+  const int R = ldu(hdr, H_R);
   if (item >= (int64_t)R * heads_per_row) return false;
   const int slot = (int)(item / heads_per_row);
   const int jh = (int)(item - (int64_t)slot * heads_per_row);
-  it.r = work[slot];
-  const int TQB = hdr[H_TQB];
+  it.r = ldu(work, slot);
+  const int TQB = ldu(hdr, H_TQB);
   const int hs = it.r / TQB;
   const int qg = it.r - hs * TQB;
   it.h = heads_per_row == 1 ? hs : hs * group + jh;
   it.g = it.h / group;
-  it.b = qb_seq[qg];
-  it.qb = qg - qbase[it.b];
-  it.q0 = seq.cu_q[it.b];
-  it.sq = (int)(seq.cu_q[it.b + 1] - it.q0);
-  it.skv = seq.seqused_kv ? seq.seqused_kv[it.b] : (int)(seq.cu_kv[it.b + 1] - seq.cu_kv[it.b]);
+  it.b = ldu(qb_seq, qg);
+  it.qb = qg - ldu(qbase, it.b);
+  it.q0 = ldu(seq.cu_q, it.b);
+  it.sq = (int)(ldu(seq.cu_q, it.b + 1) - it.q0);
+  it.skv = seq.seqused_kv ? ldu(seq.seqused_kv, it.b) : (int)(ldu(seq.cu_kv, it.b + 1) - ldu(seq.cu_kv, it.b));
   it.row_lo = it.qb * QT;
   it.nrows = min(QT, it.sq - it.row_lo);
   return true;
 }
 
-__device__ __forceinline__ KvAddr make_kv_addr(const SeqArgs& seq, const int32_t* block_table, int b, int g,
-                                               int n2, int D, int page_size, int max_pages,
-                                               int64_t page_stride) {
-  KvAddr ka;
-  ka.block_table = block_table;
-  ka.paged = seq.seqused_kv != nullptr;
-  ka.seq_row0 = ka.paged ? 0 : seq.cu_kv[b];
-  ka.bt_row = b * max_pages;
-  ka.page_size = page_size;
-  ka.page_stride = page_stride;
-  ka.row_stride = (int64_t)n2 * D;
-  ka.head_off = (int64_t)g * D;
-  return ka;
-}
-
-// Staging of a [ROWS x D] 16-bit tile: 256 threads, 16 bytes each per pass.
-template <int D, int ROWS>
+// Staging of a [ROWS x D] 16-bit tile whose rows are `row_stride` elements
+// apart: 256 threads, one 16-byte chunk each per pass.  The thread's element
+// offsets inside the tile are fixed per work item; each load takes a uniform
+// base pointer (row 0, column 0 of the tile).
+template <class L, int D, int ROWS>
 struct Stage {
   static constexpr int CH = D / 8;
   static constexpr int RPP = 256 / CH;      // rows per pass
   static constexpr int PASSES = ROWS / RPP;
   static_assert(ROWS % RPP == 0, "tile rows must fill whole passes");
   u32x4_t r[PASSES];
+  int toff[PASSES];  // global element offsets of this thread's chunks
+  int loff[PASSES];  // LDS byte offsets of this thread's chunks
 
-  // rows whose `ok(row)` is false are zero-filled; `off(row)` is the element
-  // offset of the row's column 0.
-  template <typename OffF, typename OkF>
-  __device__ __forceinline__ void load(const uint16_t* base, OffF off, OkF ok) {
+  __device__ __forceinline__ void init(int row_stride) {
     const int c = threadIdx.x % CH;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int row = p * RPP + threadIdx.x / CH;
-      r[p] = ok(row) ? gload16(base + off(row) + c * 8) : zero_u4();
+      toff[p] = (p * RPP + (int)threadIdx.x / CH) * row_stride + c * 8;
+      loff[p] = L::chunk_off(p * RPP + (int)threadIdx.x / CH, c);
+    }
+  }
+  __device__ __forceinline__ static int row_of(int p) { return p * RPP + (int)threadIdx.x / CH; }
+  // rows >= nvalid are zero-filled
+  __device__ __forceinline__ void load(const uint16_t* base, int nvalid) {
+    if (nvalid >= ROWS) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) r[p] = gload16(base + toff[p]);
+    } else {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) r[p] = row_of(p) < nvalid ? gload16(base + toff[p]) : zero_u4();
     }
   }
   __device__ __forceinline__ void store(char* lds) const {
-    const int c = threadIdx.x % CH;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = p * RPP + threadIdx.x / CH;
-      lds_write16(lds, Tile<D>::chunk_off(row, c), r[p]);
+    for (int p = 0; p < PASSES; ++p) lds_write16(lds, loff[p], r[p]);
+  }
+};
+
+// s_waitcnt on the vector-memory counter only: wait until at most N of this
+// wave's vector memory operations (loads, and loads into LDS) are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (N & 0xF) | ((N >> 4) << 14));
+}
+
+// Direct global -> LDS staging (global_load_lds_dwordx4) of a ROWS x D tile
+// with layout L.  Lane l of a wave instruction writes LDS bytes base + 16 l
+// (checked on the hardware), so instruction i fills 16-byte slots
+// 64 i .. 64 i + 63 of the tile; each lane fetches the global chunk that the
+// layout puts in its slot (pad slots fetch a harmless chunk).  The tile's
+// NINST instructions are spread over the 4 waves, PER_WAVE each.  Rows at or
+// past `nvalid` are fetched from row nvalid - 1 (finite data the kernel then
+// masks), so no lane reads outside the tensor.
+template <class L, int D, int ROWS>
+struct DmaTile {
+  static constexpr int SPR = L::ROW_BYTES / 16;  // 16-byte slots per row
+  static constexpr int NINST = ROWS * SPR / 64;
+  static constexpr int PER_WAVE = NINST / 4;
+  static_assert((ROWS * SPR) % 64 == 0 && NINST % 4 == 0, "tile must split evenly over 4 waves");
+  int row[PER_WAVE];
+  int col[PER_WAVE];
+  __device__ __forceinline__ void init() {
+    const int wv = threadIdx.x >> 6, lane = lane_id();
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int slot = 64 * (wv + 4 * j) + lane;
+      const int r = slot / SPR, c = slot % SPR;
+      int chunk;
+      if constexpr (L::LINEAR) {
+        chunk = c < L::CH ? c : 0;
+      } else {
+        chunk = c ^ L::swz(r);
+      }
+      row[j] = r;
+      col[j] = 8 * chunk;
+    }
+  }
+  // gbase: element pointer of tile row 0, column 0; rows are row_stride apart
+  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int64_t row_stride, int nvalid) const {
+    const int wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int r = min(row[j], nvalid - 1);
+      const uint16_t* src = gbase + r * row_stride + col[j];
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)(lds_tile + 1024 * (wv + 4 * j)), 16,
+                                       0, 0);
     }
   }
 };
+
+// Waits for every scalar (and LDS) load in flight and keeps the scheduler from
+// moving loads across this point.  Called after a loop's index-list reads so
+// that no scalar load -- whose results may return out of order and would force
+// full LDS waits -- is outstanding while the MFMA pipeline streams LDS reads.
+__device__ __forceinline__ void settle_scalar_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One fp32 per row of a 64-row tile, loaded by one wave into LDS (lane l ->
+// bytes 4 l); rows at or past nvalid repeat row nvalid - 1.
+__device__ __forceinline__ void dma_rows_f32(float* lds, const float* g, int64_t stride, int nvalid) {
+  const int r = min(lane_id(), nvalid - 1);
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(g + r * stride),
+                                   (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
+}
+
+// Element offset of key `key0` (row 0 of a sub-tile that stays inside one
+// page) of KV head g in sequence b: packed rows cu_kv[b] + key, or
+// (block_table[b, key / page_size], key % page_size) in the paged layout.
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_tile_offset(const SeqArgs& seq, const int32_t* block_table, int b, int g,
+                                                  int key0, int n2, int D, int page_size, int max_pages,
+                                                  int64_t page_stride) {
+  if constexpr (PAGED) {
+    const int page = ldu(block_table, (int64_t)b * max_pages + key0 / page_size);
+    return (int64_t)page * page_stride + ((int64_t)(key0 % page_size) * n2 + g) * D;
+  } else {
+    return ((ldu(seq.cu_kv, b) + key0) * n2 + g) * (int64_t)D;
+  }
+}
 
 // Walk over the 64-key sub-tiles of a CSR row: blocks cols[e0..e1), each cut
 // into by / 64 sub-tiles, keeping those whose first key is below `kend` (the
@@ -107,10 +199,10 @@ struct SubTileWalk {
     kend = kend_;
   }
   __device__ __forceinline__ bool valid() const { return e < e1; }
-  __device__ __forceinline__ int key() const { return cols[e] * by + s * KT; }
+  __device__ __forceinline__ int key() const { return ldu(cols, e) * by + s * KT; }
   __device__ __forceinline__ void next() {
     ++s;
-    if (s >= nsub || cols[e] * by + s * KT >= kend) {
+    if (s >= nsub || ldu(cols, e) * by + s * KT >= kend) {
       ++e;
       s = 0;
     }
@@ -129,18 +221,63 @@ __device__ __forceinline__ u32x4_t pack8(const f32x16_t& x, int base) {
   return r;
 }
 
-// A-operand read of a transposed 16-bit tile (rows = contraction index):
-// lane l gets rows k0 + 4 (l / 32) + {0..3} and + 8 + {0..3} of column
-// col0 + l % 32 -- the key/query-slot order that matches a C fragment packed
-// with pack8(x, 8 * (kc % 2)) for 16-row chunk kc (k0 = 16 kc).
-template <int D>
-__device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, int k0, int col0) {
-  const int lane = lane_id();
-  const int s16 = lane & 15;
-  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-  const int row = k0 + 4 * (lane >> 5) + (s16 >> 2);
-  const u32x2_t lo = lds_read_tr(lds, Tile<D>::col_off(row, col));
-  const u32x2_t hi = lds_read_tr(lds, Tile<D>::col_off(row + 8, col));
+// Per-lane LDS byte offsets of the two MFMA operand read patterns of a
+// row-major tile with layout L, for reads whose first row is a multiple of 16:
+//  * rd(kk): rows row0 + lane % 32, columns 16 kk + 8 (lane / 32) .. + 7 (an
+//    A or B operand over D, ds_read_b128); add row0 * ROW_BYTES.
+//  * tr(mt, h): the transposed read -- source lane s of each 16-lane group
+//    points at row k0 + 4 (lane / 32) + s / 4 + 8 h, columns 32 mt + 16 ((lane
+//    / 16) % 2) + 4 (s % 4) .. + 3, so lane l receives rows k0 + 4 (l / 32) +
+//    8 h + {0..3} of column 32 mt + l % 32.  Add k0 * ROW_BYTES.  The two
+//    reads h = 0, 1 form an A operand whose 8 k-slots match a C fragment
+//    packed by pack8(x, 8 (kc % 2)) for the 16-row chunk k0 = 16 kc.
+// Linear layouts keep one base per pattern (the rest are immediates); the
+// XOR layout keeps every offset.
+template <class L, int D, bool LIN = L::LINEAR>
+struct Operands;
+
+template <class L, int D>
+struct Operands<L, D, true> {
+  int rb, tb;
+  __device__ __forceinline__ void init() {
+    const int lane = lane_id(), s16 = lane & 15;
+    rb = L::chunk_off(lane & 31, lane >> 5);
+    tb = L::col_off(4 * (lane >> 5) + (s16 >> 2), 16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+  }
+  __device__ __forceinline__ int rd(int kk) const { return rb + 32 * kk; }
+  __device__ __forceinline__ int tr(int mt, int h) const { return tb + 64 * mt + 8 * h * L::ROW_BYTES; }
+};
+
+template <class L, int D>
+struct Operands<L, D, false> {
+  int rd_[D / 16];
+  int tr_[D / 32][2];
+  __device__ __forceinline__ void init() {
+    const int lane = lane_id(), s16 = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) rd_[kk] = L::chunk_off(lane & 31, 2 * kk + (lane >> 5));
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        tr_[mt][h] = L::col_off(4 * (lane >> 5) + (s16 >> 2) + 8 * h,
+                                32 * mt + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+  }
+  __device__ __forceinline__ int rd(int kk) const { return rd_[kk]; }
+  __device__ __forceinline__ int tr(int mt, int h) const { return tr_[mt][h]; }
+};
+
+// A/B operand (rows row0 + lane % 32) via ds_read_b128.
+template <class L, int D>
+__device__ __forceinline__ u32x4_t read_operand(const char* lds, const Operands<L, D>& of, int row0, int kk) {
+  return lds_read16(lds + row0 * L::ROW_BYTES, of.rd(kk));
+}
+// A operand of the transposed tile for the 16-row chunk k0 = 16 kc, columns 32 mt ..
+template <class L, int D>
+__device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, const Operands<L, D>& of, int k0, int mt) {
+  const char* base = lds + k0 * L::ROW_BYTES;
+  const u32x2_t lo = lds_read_tr(base, of.tr(mt, 0));
+  const u32x2_t hi = lds_read_tr(base, of.tr(mt, 1));
   u32x4_t r;
   r.x = lo.x;
   r.y = lo.y;
@@ -149,12 +286,22 @@ __device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, int k0, int 
   return r;
 }
 
-// A/B-operand read of a row-major tile: lane l gets row row0 + l % 32,
-// columns 16 kk + 8 (l / 32) .. + 7.
-template <int D>
-__device__ __forceinline__ u32x4_t read_operand(const char* lds, int row0, int kk) {
-  const int lane = lane_id();
-  return lds_read16(lds, Tile<D>::chunk_off(row0 + (lane & 31), 2 * kk + (lane >> 5)));
+// Runs N MFMA steps whose A (or B) operands come from LDS: step i's operand
+// is read by read(i) LOOK steps before mfma(i, operand) consumes it, and the
+// order is pinned with scheduling barriers, so each MFMA finds its operand
+// already loaded instead of waiting out the LDS latency.
+template <int N, int LOOK, class ReadF, class MfmaF>
+__device__ __forceinline__ void mfma_pipeline(ReadF read, MfmaF mfma) {
+  u32x4_t ring[LOOK];
+#pragma unroll
+  for (int i = 0; i < LOOK; ++i) ring[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const u32x4_t a = ring[i % LOOK];
+    if (i + LOOK < N) ring[i % LOOK] = read(i + LOOK);
+    mfma(i, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Stores a [32 x 32] C fragment holding X^T (rows = feature d, columns =

@@ -45,15 +45,22 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 //   S^T = K Q^T, dP^T = V dO^T            (K, V row-major from LDS)
 //   P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T o (dP^T - D)
 //   dQ^T += K^T dS^T                       (K^T via LDS transpose loads)
+constexpr int DQ_STAGES = 4;  // LDS ring depth: K/V sub-tiles loaded 3 ahead
+
 template <typename MF, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
-  constexpr int TILE = KT * D * 2;
+  using L = XorTile<D>;  // K: read row-major (S^T) and transposed (dQ^T); V: row-major (dP^T)
+  constexpr int TILE = L::template bytes<KT>();
+  constexpr int STAGE = 2 * TILE;
   constexpr int NMT = D / 32;
   constexpr int NKK = D / 16;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  using Dma = DmaTile<L, D, KT>;
+  constexpr int OPS = 2 * Dma::PER_WAVE;  // vector-memory operations per staged sub-tile and wave
+  __shared__ __attribute__((aligned(16))) char smem[DQ_STAGES * STAGE];
 
   QItem it;
-  if (!decode_qitem(blockIdx.x, a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it)) return;
+  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
+    return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int my_local = wv * 32 + (lane & 31);
   const int my_row = it.row_lo + my_local;
@@ -74,65 +81,73 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
   const float lse2 = row_ok ? a.lse[tok * a.n1 + it.h] * LOG2E : INFINITY;
   const float dl = row_ok ? a.dl[tok * a.n1 + it.h] : 0.f;
 
-  const KvAddr ka = make_kv_addr(a.seq, nullptr, it.b, it.g, a.n2, D, 0, 0, 0);
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
-
   f32x16_t acc[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) acc[mt] = zero16();
   const float c2 = a.sigma_log2e;
+  const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
 
-  Stage<D, KT> sk, sv;
-  SubTileWalk wk;
-  wk.init(a.cols, a.row_ptr[it.r], a.row_ptr[it.r + 1], a.seq.by, kend);
-  auto load = [&](int key0) {
-    auto off = [&](int row) { return ka.offset(key0 + row); };
-    auto ok = [&](int row) { return key0 + row < it.skv; };
-    sk.load(kp, off, ok);
-    sv.load(vp, off, ok);
+  Dma dma;
+  dma.init();
+  Operands<L, D> of;
+  of.init();
+  // `ld` issues sub-tile loads DQ_STAGES - 1 ahead of `cp`, which computes
+  SubTileWalk ld, cp;
+  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
+  cp = ld;
+  auto issue = [&](int stage) {
+    char* st = smem + stage * STAGE;
+    const int key0 = ld.key();
+    const int64_t off = kv_tile_offset<false>(a.seq, nullptr, it.b, it.g, key0, a.n2, D, 0, 0, 0);
+    dma.issue(st, kp + off, (int64_t)a.n2 * D, it.skv - key0);
+    dma.issue(st + TILE, vp + off, (int64_t)a.n2 * D, it.skv - key0);
+    ld.next();
   };
-  if (wk.valid()) load(wk.key());
-  int buf = 0;
-  while (wk.valid()) {
-    const int key0 = wk.key();
-    char* kl = smem + buf * 2 * TILE;
-    char* vl = kl + TILE;
-    sk.store(kl);
-    sv.store(vl);
-    __syncthreads();
-    wk.next();
-    if (wk.valid()) load(wk.key());
-
-    f32x16_t s[2], dp[2];
+  int nld = 0;
+  while (ld.valid() && nld < DQ_STAGES - 1) issue(nld++);
+  int ahead = nld - 1;
+  int stage = 0;
+  while (cp.valid()) {
+    if (ahead >= 2) wait_vmcnt<2 * OPS>();
+    else if (ahead == 1) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's loads landed; the stage reloaded below is free
+    if (ld.valid())
+      issue((stage + DQ_STAGES - 1) % DQ_STAGES);
+    else
+      --ahead;
+    const int key0 = cp.key();
+    cp.next();
+    settle_scalar_loads();
+    const char* kl = smem + stage * STAGE;
+    const char* vl = kl + TILE;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-      dp[t] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s[t] = MF::mfma(read_operand<D>(kl, 32 * t, kk), qf[kk], s[t]);
-        dp[t] = MF::mfma(read_operand<D>(vl, 32 * t, kk), df[kk], dp[t]);
-      }
-    }
-    const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {  // 32-key halves of the sub-tile
+      f32x16_t s = zero16(), dp = zero16();
+      // step i: kk = i / 2; even = S^T (K rows), odd = dP^T (V rows)
+      mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? vl : kl, of, 32 * t, i >> 1); },
+                                [&](int i, const u32x4_t& op) {
+                                  if (i & 1)
+                                    dp = MF::mfma(op, df[i >> 1], dp);
+                                  else
+                                    s = MF::mfma(op, qf[i >> 1], s);
+                                });
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        float p = fast_exp2(fmaf(s[t][i], c2, -lse2));
+        float p = fast_exp2(fmaf(s[i], c2, -lse2));
         if (key > lim) p = 0.f;
-        s[t][i] = p * (dp[t][i] - dl);  // dS^T
+        s[i] = p * (dp[i] - dl);  // dS^T
       }
-    u32x4_t db[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) db[kc] = pack8<MF>(s[kc >> 1], 8 * (kc & 1));
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) acc[mt] = MF::mfma(read_tr_operand<D>(kl, 16 * kc, 32 * mt), db[kc], acc[mt]);
-    buf ^= 1;
+      const u32x4_t db0 = pack8<MF>(s, 0), db1 = pack8<MF>(s, 8);
+      // step i: kc = 2 t + i / NMT, mt = i % NMT
+      mfma_pipeline<2 * NMT, 4>(
+          [&](int i) { return read_tr_operand(kl, of, 16 * (2 * t + i / NMT), i % NMT); },
+          [&](int i, const u32x4_t& op) { acc[i % NMT] = MF::mfma(op, (i < NMT) ? db0 : db1, acc[i % NMT]); });
+    }
+    stage = (stage + 1) % DQ_STAGES;
   }
   if (row_ok) {
     uint16_t* op = reinterpret_cast<uint16_t*>(a.dq) + tok * qstride + (int64_t)it.h * D;
@@ -153,26 +168,79 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 //                                      P / dS straight from registers)
 constexpr int QS = 64;  // query rows per staged sub-tile
 
+// Walk over (q-head of the group, q-block of the tile's column list, 64-row
+// half of the q-block), skipping halves past the sequence end or entirely
+// above the causal limit of the tile's first key.
+struct ColWalk {
+  const int32_t* col_ptr;
+  const int32_t* qrows;
+  int hh, e, e1, half;
+  int group, per_head, g, tkb, kg, sq, qoff, key_min, causal;
+  __device__ __forceinline__ int col(int h) const { return (per_head ? g * group + h : g) * tkb + kg; }
+  __device__ __forceinline__ bool ok(int qb, int hf) const {
+    const int r0 = qb * 128 + hf * QS;
+    if (r0 >= sq) return false;
+    if (causal && min(r0 + QS, sq) - 1 + qoff < key_min) return false;
+    return true;
+  }
+  __device__ __forceinline__ void open(int h) {
+    const int c = col(h);
+    e = ldu(col_ptr, c);
+    e1 = ldu(col_ptr, c + 1);
+  }
+  __device__ __forceinline__ void settle() {
+    while (hh < group) {
+      while (e < e1) {
+        const int qb = ldu(qrows, e);
+        while (half < 2) {
+          if (ok(qb, half)) return;
+          ++half;
+        }
+        ++e;
+        half = 0;
+      }
+      ++hh;
+      if (hh < group) open(hh);
+    }
+  }
+  __device__ __forceinline__ bool valid() const { return hh < group; }
+  __device__ __forceinline__ void next() {
+    ++half;
+    settle();
+  }
+  __device__ __forceinline__ int row0() const { return ldu(qrows, e) * 128 + half * QS; }
+};
+
+constexpr int DKDV_STAGES = 4;  // LDS ring depth: Q/dO tiles loaded 3 sub-tiles ahead
+
 template <typename MF, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
-  constexpr int TILE = QS * D * 2;
+  using QL = XorTile<D>;  // Q and dO: read row-major (S, dP) and transposed (dK^T, dV^T)
+  constexpr int TILE = QL::template bytes<QS>();
+  constexpr int STAGE = 2 * TILE + 2 * QS * 4;  // Q, dO, lse, D
   constexpr int NMT = D / 32;
   constexpr int NKK = D / 16;
-  constexpr int BUF = 2 * TILE + 2 * QS * 4;  // Q, dO, lse*log2e, D
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  using Dma = DmaTile<QL, D, QS>;
+  // vector-memory operations per staged tile for this wave: Q and dO chunks,
+  // plus the lse row (wave 0) or the D row (wave 1)
+  constexpr int OPS_LO = 2 * Dma::PER_WAVE + 1;  // waves 0, 1
+  constexpr int OPS_HI = 2 * Dma::PER_WAVE;      // waves 2, 3
+  __shared__ __attribute__((aligned(16))) char smem[DKDV_STAGES * STAGE];
 
-  const int KVI = a.hdr[H_KVITEMS];
-  const int64_t item = blockIdx.x / a.sub_tiles;
-  const int sub = blockIdx.x - (int)item * a.sub_tiles;
+  const int KVI = ldu(a.hdr, H_KVITEMS);
+  const int64_t flat = xcd_item(blockIdx.x);
+  const int64_t item = flat / a.sub_tiles;
+  const int sub = (int)(flat - item * a.sub_tiles);
   if (item >= KVI) return;
-  const int TKB = a.hdr[H_TKB];
-  const int w_id = a.work_kv[item];
+  const int TKB = ldu(a.hdr, H_TKB);
+  const int w_id = ldu(a.work_kv, item);
   const int g = w_id / TKB, kg = w_id - g * TKB;
-  const int b = a.kb_seq[kg];
-  const int kb = kg - a.kbase[b];
-  const int64_t q0 = a.seq.cu_q[b];
-  const int sq = (int)(a.seq.cu_q[b + 1] - q0);
-  const int skv = (int)(a.seq.cu_kv[b + 1] - a.seq.cu_kv[b]);
+  const int b = ldu(a.kb_seq, kg);
+  const int kb = kg - ldu(a.kbase, b);
+  const int64_t q0 = ldu(a.seq.cu_q, b);
+  const int sq = (int)(ldu(a.seq.cu_q, b + 1) - q0);
+  const int64_t kv0 = ldu(a.seq.cu_kv, b);
+  const int skv = (int)(ldu(a.seq.cu_kv, b + 1) - kv0);
   const int key_lo = kb * a.seq.by + sub * 128;
   if (key_lo >= skv) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -180,7 +248,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
   const bool key_ok = my_key < skv;
   const int qoff = skv - sq;
   const int64_t kvstride = (int64_t)a.n2 * D;
-  const int64_t krow = (a.seq.cu_kv[b] + my_key) * kvstride + (int64_t)g * D + 8 * (lane >> 5);
+  const int64_t krow = (kv0 + my_key) * kvstride + (int64_t)g * D + 8 * (lane >> 5);
   u32x4_t kf[NKK], vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -197,121 +265,93 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
   const int64_t qstride = (int64_t)a.n1 * D;
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* dop = reinterpret_cast<const uint16_t*>(a.dout);
-  // smallest key of this workgroup's tile: q rows whose causal limit is below
-  // it contribute nothing
-  const int wg_key_min = key_lo;
 
-  // Walk: heads h of group g, q-blocks of column c(h), 64-row halves.
-  struct Walk {
-    int hh, e, e1, half;
-  } wk;
-  const int ncols_heads = a.hs == a.n1 ? a.group : 1;  // distinct columns in the group
-  auto col_of = [&](int hh) { return (a.hs == a.n1 ? g * a.group + hh : g) * TKB + kg; };
-  auto sub_ok = [&](int qb, int half) {
-    const int r0 = qb * 128 + half * QS;
-    if (r0 >= sq) return false;
-    if (CAUSAL) {
-      const int rlast = min(r0 + QS, sq) - 1;
-      if (rlast + qoff < wg_key_min) return false;
-    }
-    return true;
+  // Two cursors over the same (head, q-block, half) sequence: `ld` issues the
+  // loads DKDV_STAGES - 1 tiles ahead of `cp`, which computes.
+  ColWalk ld, cp;
+  ld.col_ptr = a.col_ptr;
+  ld.qrows = a.qrows;
+  ld.group = a.group;
+  ld.per_head = a.hs == a.n1;
+  ld.g = g;
+  ld.tkb = TKB;
+  ld.kg = kg;
+  ld.sq = sq;
+  ld.qoff = qoff;
+  ld.key_min = key_lo;
+  ld.causal = CAUSAL;
+  ld.hh = 0;
+  ld.half = 0;
+  ld.open(0);
+  ld.settle();
+  cp = ld;
+
+  Dma dma;
+  dma.init();
+  Operands<QL, D> of;
+  of.init();
+  auto issue = [&](int stage) {
+    char* st = smem + stage * STAGE;
+    const int h = g * a.group + ld.hh;
+    const int r0 = ld.row0();
+    const int nvalid = sq - r0;
+    const int64_t off = (q0 + r0) * qstride + (int64_t)h * D;
+    dma.issue(st, qp + off, qstride, nvalid);
+    dma.issue(st + TILE, dop + off, qstride, nvalid);
+    float* stat = reinterpret_cast<float*>(st + 2 * TILE);
+    if (wv == 0) dma_rows_f32(stat, a.lse + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    if (wv == 1) dma_rows_f32(stat + QS, a.dl + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    ld.next();
   };
-  // advance to the first valid (head, entry, half) at or after the current one
-  auto settle = [&]() {
-    while (wk.hh < a.group) {
-      while (wk.e < wk.e1) {
-        const int qb = a.qrows[wk.e];
-        while (wk.half < 2) {
-          if (sub_ok(qb, wk.half)) return;
-          ++wk.half;
-        }
-        ++wk.e;
-        wk.half = 0;
-      }
-      ++wk.hh;
-      if (wk.hh < a.group) {
-        const int c = col_of(ncols_heads == 1 ? 0 : wk.hh);
-        wk.e = a.col_ptr[c];
-        wk.e1 = a.col_ptr[c + 1];
-      }
-    }
-  };
-  {
-    const int c = col_of(0);
-    wk.hh = 0;
-    wk.e = a.col_ptr[c];
-    wk.e1 = a.col_ptr[c + 1];
-    wk.half = 0;
+
+  int ahead = 0;  // tiles issued beyond the one being computed
+  int stage_ld = 0;
+  while (ld.valid() && stage_ld < DKDV_STAGES - 1) {
+    issue(stage_ld);
+    ++stage_ld;
   }
-  settle();
-  auto advance = [&]() {
-    ++wk.half;
-    settle();
-  };
-
-  Stage<D, QS> sq_, sd_;
-  float st_lse = 0.f, st_dl = 0.f;
-  int cur_r0 = 0, cur_h = 0;
-  auto load = [&]() {
-    const int h = g * a.group + wk.hh;
-    const int r0 = a.qrows[wk.e] * 128 + wk.half * QS;
-    auto off = [&](int row) { return (q0 + r0 + row) * qstride + (int64_t)h * D; };
-    auto ok = [&](int row) { return r0 + row < sq; };
-    sq_.load(qp, off, ok);
-    sd_.load(dop, off, ok);
-    const int t = threadIdx.x;
-    if (t < 2 * QS) {
-      const int row = t & (QS - 1);
-      const bool rok = r0 + row < sq;
-      const int64_t idx = (q0 + r0 + row) * a.n1 + h;
-      if (t < QS)
-        st_lse = rok ? a.lse[idx] * LOG2E : INFINITY;
-      else
-        st_dl = rok ? a.dl[idx] : 0.f;
+  ahead = stage_ld - 1;
+  int stage = 0;
+  while (cp.valid()) {
+    // this wave's loads for the current tile are done once at most `ahead`
+    // tiles' worth of its operations are still in flight
+    if (wv < 2) {
+      if (ahead >= 2) wait_vmcnt<2 * OPS_LO>();
+      else if (ahead == 1) wait_vmcnt<OPS_LO>();
+      else wait_vmcnt<0>();
+    } else {
+      if (ahead >= 2) wait_vmcnt<2 * OPS_HI>();
+      else if (ahead == 1) wait_vmcnt<OPS_HI>();
+      else wait_vmcnt<0>();
     }
-    cur_r0 = r0;
-    cur_h = h;
-  };
-
-  int buf = 0;
-  int ld_r0 = 0;
-  if (wk.hh < a.group) {
-    load();
-    ld_r0 = cur_r0;
-  }
-  while (wk.hh < a.group) {
-    const int r0 = ld_r0;
-    char* ql = smem + buf * BUF;
+    __builtin_amdgcn_s_barrier();  // every wave's loads landed; the stage freed below is no longer read
+    if (ld.valid()) {
+      issue((stage + DKDV_STAGES - 1) % DKDV_STAGES);
+    } else {
+      --ahead;
+    }
+    const int r0 = cp.row0();
+    const int nrows = sq - r0;  // valid rows of this tile (may exceed QS)
+    cp.next();
+    settle_scalar_loads();
+    char* ql = smem + stage * STAGE;
     char* dl_ = ql + TILE;
-    float* lsel = reinterpret_cast<float*>(ql + 2 * TILE);
-    float* dll = lsel + QS;
-    sq_.store(ql);
-    sd_.store(dl_);
-    if (threadIdx.x < QS)
-      lsel[threadIdx.x] = st_lse;
-    else if (threadIdx.x < 2 * QS)
-      dll[threadIdx.x - QS] = st_dl;
-    __syncthreads();
-    advance();
-    if (wk.hh < a.group) {
-      load();
-      ld_r0 = cur_r0;
-    }
+    const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
+    const float* dll = lsel + QS;
 
-    // S[qrow, key], dP[qrow, key] for 64 query rows (two 32-row tiles)
-    f32x16_t s[2], dp[2];
+    const bool tail = nrows < QS;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-      dp[t] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s[t] = MF::mfma(read_operand<D>(ql, 32 * t, kk), kf[kk], s[t]);
-        dp[t] = MF::mfma(read_operand<D>(dl_, 32 * t, kk), vf[kk], dp[t]);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {  // 32-row halves of the q sub-tile
+      // S[qrow, key], dP[qrow, key] for query rows 32 t .. 32 t + 31
+      f32x16_t s = zero16(), dp = zero16();
+      // step i: kk = i / 2; even = S (Q rows), odd = dP (dO rows)
+      mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * t, i >> 1); },
+                                [&](int i, const u32x4_t& op) {
+                                  if (i & 1)
+                                    dp = MF::mfma(op, vf[i >> 1], dp);
+                                  else
+                                    s = MF::mfma(op, kf[i >> 1], s);
+                                });
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         const int rl = 32 * t + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
@@ -320,30 +360,31 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * ig + j;
-          float p = fast_exp2(fmaf(s[t][i], c2, -__uint_as_float(l4[j])));
+          float p = fast_exp2(fmaf(s[i], c2, -__uint_as_float(l4[j]) * LOG2E));
           if (CAUSAL && my_key > r0 + rl + j + qoff) p = 0.f;
-          s[t][i] = p;
-          dp[t][i] = p * (dp[t][i] - __uint_as_float(d4[j]));
+          if (tail && rl + j >= nrows) p = 0.f;
+          s[i] = p;
+          dp[i] = p * (dp[i] - __uint_as_float(d4[j]));
         }
       }
-    u32x4_t pb[4], sb[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      pb[kc] = pack8<MF>(s[kc >> 1], 8 * (kc & 1));
-      sb[kc] = pack8<MF>(dp[kc >> 1], 8 * (kc & 1));
+      const u32x4_t pb0 = pack8<MF>(s, 0), pb1 = pack8<MF>(s, 8);
+      const u32x4_t sb0 = pack8<MF>(dp, 0), sb1 = pack8<MF>(dp, 8);
+      // step i: kc = 2 t + i / (2 NMT), mt = (i / 2) % NMT; even = dV^T, odd = dK^T
+      mfma_pipeline<4 * NMT, 4>(
+          [&](int i) { return read_tr_operand((i & 1) ? ql : dl_, of, 16 * (2 * t + i / (2 * NMT)), (i >> 1) % NMT); },
+          [&](int i, const u32x4_t& op) {
+            const bool lo = i < 2 * NMT;
+            const int mt = (i >> 1) % NMT;
+            if (i & 1)
+              dk[mt] = MF::mfma(op, lo ? sb0 : sb1, dk[mt]);
+            else
+              dv[mt] = MF::mfma(op, lo ? pb0 : pb1, dv[mt]);
+          });
     }
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        dv[mt] = MF::mfma(read_tr_operand<D>(dl_, 16 * kc, 32 * mt), pb[kc], dv[mt]);
-        dk[mt] = MF::mfma(read_tr_operand<D>(ql, 16 * kc, 32 * mt), sb[kc], dk[mt]);
-      }
-    buf ^= 1;
+    stage = (stage + 1) % DKDV_STAGES;
   }
-  (void)cur_h;
   if (key_ok) {
-    const int64_t orow = (a.seq.cu_kv[b] + my_key) * kvstride + (int64_t)g * D;
+    const int64_t orow = (kv0 + my_key) * kvstride + (int64_t)g * D;
     uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + orow;
     uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + orow;
 #pragma unroll

@@ -73,30 +73,49 @@ __device__ __forceinline__ f32x16_t zero16() {
 }
 
 // ---------------------------------------------------------------------------
-// Row-major LDS tiles of 16-bit elements, `D` columns per row, stored in
-// 16-byte chunks whose position inside the row is XOR-permuted by the row
-// index so that the MFMA operand reads (32 rows at one chunk, or 8 rows x 4
-// chunks for the transposed reads) spread over the LDS banks.
+// Row-major LDS tiles of 16-bit elements with D columns.  Two layouts:
+//
+// XorTile: rows of 2D bytes whose 16-byte chunks are XOR-permuted by row % 16.
+//   ds_read_b128 is served 16 lanes at a time; 16 consecutive rows reading the
+//   same logical chunk land on 16 distinct 16-byte bank groups, and the
+//   transposed ds_read_b64_tr_b16 reads (4 rows x 32 bytes per 16 lanes) stay
+//   conflict free too.  For tiles read both ways.  Offsets are non-linear in
+//   the column, so kernels precompute them per lane (OperandOffsets).
+//
+// PadTile: rows padded by PAD bytes, addresses linear in row and column.  With
+//   64 banks of 4 bytes, PAD = 16 puts 16 consecutive rows at 16 distinct bank
+//   groups (row-major operand reads); PAD = 64 makes the 4 rows of a
+//   transposed read cover 16 distinct bank groups.  For tiles read one way.
 // ---------------------------------------------------------------------------
 template <int D>
-struct Tile {
-  static constexpr int CH = D / 8;             // 16-byte chunks per row
+struct XorTile {
+  static constexpr int CH = D / 8;  // 16-byte chunks per row
   static constexpr int ROW_BYTES = D * 2;
+  static constexpr bool LINEAR = false;
+  template <int ROWS>
+  static constexpr int bytes() { return ROWS * ROW_BYTES; }
   static __device__ __forceinline__ int swz(int row) {
     if constexpr (CH == 16) {
       return ((row & 3) << 2) | ((row >> 2) & 3);
     } else {
-      return row & (CH - 1);
+      return (row >> 1) & (CH - 1);
     }
   }
-  // byte offset of 16-byte chunk `c` of `row`
-  static __device__ __forceinline__ int chunk_off(int row, int c) {
-    return row * ROW_BYTES + ((c ^ swz(row)) << 4);
-  }
-  // byte offset of column `col` (multiple of 4) of `row`
+  static __device__ __forceinline__ int chunk_off(int row, int c) { return row * ROW_BYTES + ((c ^ swz(row)) << 4); }
   static __device__ __forceinline__ int col_off(int row, int col) {
     return row * ROW_BYTES + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
   }
+};
+
+template <int D, int PAD>
+struct PadTile {
+  static constexpr int CH = D / 8;
+  static constexpr int ROW_BYTES = D * 2 + PAD;
+  static constexpr bool LINEAR = true;
+  template <int ROWS>
+  static constexpr int bytes() { return ROWS * ROW_BYTES; }
+  static __device__ __forceinline__ int chunk_off(int row, int c) { return row * ROW_BYTES + (c << 4); }
+  static __device__ __forceinline__ int col_off(int row, int col) { return row * ROW_BYTES + (col << 1); }
 };
 
 __device__ __forceinline__ u32x4_t lds_read16(const char* base, int off) {
@@ -117,6 +136,15 @@ __device__ __forceinline__ u32x4_t gload16(const void* p) {
 __device__ __forceinline__ u32x4_t zero_u4() {
   u32x4_t z = {0u, 0u, 0u, 0u};
   return z;
+}
+
+// Loads of read-only schedule data (index lists, lengths, page tables) with a
+// wave-uniform address, through the constant address space so they become
+// scalar loads: they are then counted apart from the vector loads, and waiting
+// for one never waits for tile loads in flight.
+template <typename T>
+__device__ __forceinline__ T ldu(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)(p))[i];
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -146,24 +174,5 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   }
   return x;
 }
-
-// Paged or packed location of a key row: element offset of (key, head g, 0).
-struct KvAddr {
-  const int32_t* block_table;
-  int64_t seq_row0;     // TND: cu_kv[b]; unused when paged
-  int64_t page_stride;  // elements
-  int32_t bt_row;       // b * max_pages
-  int32_t page_size;
-  int32_t paged;
-  int64_t row_stride;   // N2 * D
-  int64_t head_off;     // g * D
-  __device__ __forceinline__ int64_t offset(int key) const {
-    if (paged) {
-      const int page = block_table[bt_row + key / page_size];
-      return (int64_t)page * page_stride + (int64_t)(key % page_size) * row_stride + head_off;
-    }
-    return (seq_row0 + key) * row_stride + head_off;
-  }
-};
 
 }  // namespace bsa

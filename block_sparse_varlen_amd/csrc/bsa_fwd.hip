@@ -21,20 +21,35 @@
 //                          straight from the S^T accumulator registers)
 // so no score ever leaves registers and the rescale by exp(m_old - m_new) is
 // a per-lane multiply.
+#include <type_traits>
+
 #include "bsa_attn.h"
 
 namespace bsa {
 namespace {
 
-template <typename MF, int D, bool CAUSAL>
+// Softmax rescale threshold (log2 units): the running maximum used for the
+// exponentials is only moved when a row's new maximum exceeds it by more than
+// this, so exp2 arguments stay <= RESCALE_LOG2 (P <= 256) and the O^T rescale
+// is skipped for most sub-tiles.  Any reference maximum gives the same O and
+// lse; only the rounding differs.
+constexpr float RESCALE_LOG2 = 8.f;
+
+template <typename MF, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
-  constexpr int TILE = KT * D * 2;  // bytes of one K or V sub-tile
-  constexpr int NMT = D / 32;       // 32-row feature tiles of O^T
-  constexpr int NKK = D / 16;       // contraction steps over D
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  // K is read row-major only, V transposed only: each gets the padded layout
+  // that keeps its one read pattern free of bank conflicts.
+  using KL = PadTile<D, 16>;
+  using VL = PadTile<D, 64>;
+  constexpr int KTILE = KL::template bytes<KT>();
+  constexpr int VTILE = VL::template bytes<KT>();
+  constexpr int BUF = KTILE + VTILE;
+  constexpr int NMT = D / 32;  // 32-row feature tiles of O^T
+  constexpr int NKK = D / 16;  // contraction steps over D
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
   QItem it;
-  if (!decode_qitem(blockIdx.x, a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it)) return;
+  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it)) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int my_local = wv * 32 + (lane & 31);  // row within the item
   const int my_row = it.row_lo + my_local;     // row within the sequence
@@ -51,31 +66,39 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = row_ok ? gload16(qp + 16 * kk) : zero_u4();
 
-  const KvAddr ka = make_kv_addr(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   const uint16_t* kbase_p = reinterpret_cast<const uint16_t*>(a.k);
   const uint16_t* vbase_p = reinterpret_cast<const uint16_t*>(a.v);
 
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;  // reference maximum of this lane's row (raw scores)
+  float l_run = 0.f;        // this lane's partial row sum relative to m_run
   const float c2 = a.sigma_log2e;
+  const float thresh = RESCALE_LOG2 / c2;
 
-  Stage<D, KT> sk, sv;
+  Stage<KL, D, KT> sk;
+  Stage<VL, D, KT> sv;
+  sk.init(a.n2 * D);
+  sv.init(a.n2 * D);
   SubTileWalk wk;
-  wk.init(a.cols, a.row_ptr[it.r], a.row_ptr[it.r + 1], a.seq.by, kend);
+  wk.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
   auto load = [&](int key0) {
-    auto off = [&](int row) { return ka.offset(key0 + row); };
-    auto ok = [&](int row) { return key0 + row < it.skv; };
-    sk.load(kbase_p, off, ok);
-    sv.load(vbase_p, off, ok);
+    const int64_t off = kv_tile_offset<PAGED>(a.seq, a.block_table, it.b, it.g, key0, a.n2, D, a.page_size,
+                                              a.max_pages, a.page_stride);
+    const int nvalid = it.skv - key0;
+    sk.load(kbase_p + off, nvalid);
+    sv.load(vbase_p + off, nvalid);
   };
-  if (wk.valid()) load(wk.key());
-  int buf = 0;
-  while (wk.valid()) {
+  Operands<KL, D> ofk;
+  Operands<VL, D> ofv;
+  ofk.init();
+  ofv.init();
+  // One 64-key sub-tile computed from LDS buffer `buf` (0/1).
+  auto step = [&](int buf) {
+    char* kl = smem + buf * BUF;
+    char* vl = kl + KTILE;
     const int key0 = wk.key();
-    char* kl = smem + buf * 2 * TILE;
-    char* vl = kl + TILE;
     sk.store(kl);
     sv.store(vl);
     __syncthreads();
@@ -84,13 +107,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 
     // ---- S^T = K Q^T for keys key0 .. key0+63 (two 32-key tiles) ----
     f32x16_t s[2];
+    s[0] = zero16();
+    s[1] = zero16();
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[t] = MF::mfma(read_operand<D>(kl, 32 * t, kk), qf[kk], s[t]);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4_t a0 = read_operand(kl, ofk, 0, kk);
+      const u32x4_t a1 = read_operand(kl, ofk, 32, kk);
+      s[0] = MF::mfma(a0, qf[kk], s[0]);
+      s[1] = MF::mfma(a1, qf[kk], s[1]);
     }
-    // ---- masks: keys past Skv, causal limit ----
+    // ---- masks: keys past Skv, causal limit (edge sub-tiles only) ----
     const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
     if (edge) {
       const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
@@ -109,9 +135,19 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
     mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new * c2;
-    const float alpha = fast_exp2(m_run * c2 - m_use);
+    // move the reference maximum only when it is exceeded by more than the threshold
+    const bool upd = mx > m_run + thresh || (m_run == -INFINITY && mx > -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float m_new = upd ? mx : m_run;
+      const float alpha = upd ? fast_exp2((m_run - m_new) * c2) : 1.f;  // m_run = -inf -> 0
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run * c2;
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -121,24 +157,26 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
         s[t][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
+    l_run += psum;
     // ---- O^T += V^T P^T ----
     u32x4_t pb[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) pb[kc] = pack8<MF>(s[kc >> 1], 8 * (kc & 1));
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) o[mt] = MF::mfma(read_tr_operand<D>(vl, 16 * kc, 32 * mt), pb[kc], o[mt]);
+      for (int mt = 0; mt < NMT; ++mt) o[mt] = MF::mfma(read_tr_operand(vl, ofv, 16 * kc, mt), pb[kc], o[mt]);
+  };
+  if (wk.valid()) load(wk.key());
+  int buf = 0;
+  while (wk.valid()) {
+    step(buf);
     buf ^= 1;
   }
 
   // ---- epilogue: O = O^T / l, lse = scale * m + ln l ----
+  // The two half-waves share m_run (the maximum is exchanged before use), so
+  // their partial sums add directly.
   const float l_tot = l_run + wave_xor32(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -152,13 +190,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   }
 }
 
-template <typename MF, int D>
+template <typename MF, int D, bool PAGED>
 hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t st) {
   if (a.seq.causal)
-    k_fwd<MF, D, true><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_fwd<MF, D, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
   else
-    k_fwd<MF, D, false><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_fwd<MF, D, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
   return hipGetLastError();
+}
+
+template <typename MF, int D>
+hipError_t launch_p(const FwdArgs& a, int64_t grid, hipStream_t st) {
+  return a.seq.seqused_kv ? launch_t<MF, D, true>(a, grid, st) : launch_t<MF, D, false>(a, grid, st);
 }
 
 }  // namespace
@@ -166,8 +209,8 @@ hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t st) {
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   const bool bf = dtype == 2;
-  if (head_dim == 128) return bf ? launch_t<BF16, 128>(a, grid, st) : launch_t<F16, 128>(a, grid, st);
-  return bf ? launch_t<BF16, 64>(a, grid, st) : launch_t<F16, 64>(a, grid, st);
+  if (head_dim == 128) return bf ? launch_p<BF16, 128>(a, grid, st) : launch_p<F16, 128>(a, grid, st);
+  return bf ? launch_p<BF16, 64>(a, grid, st) : launch_p<F16, 64>(a, grid, st);
 }
 
 }  // namespace bsa

@@ -21,6 +21,11 @@ enum HeaderSlot {
 
 enum SparseKind { SP_NONE = 0, SP_MASK = 1, SP_SABI = 2, SP_IDX = 3 };
 
+// Attention work items are handed to the 8 XCDs in runs of XCD_SEG
+// consecutive items (xcd_item in bsa_attn.h); grids are padded to whole rounds.
+constexpr int NUM_XCD = 8;
+constexpr int XCD_SEG = 32;
+
 // Host-known upper bounds that size every workspace region.
 struct Bounds {
   int64_t qbar;      // >= total q-blocks
