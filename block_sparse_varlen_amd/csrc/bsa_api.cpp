@@ -122,7 +122,10 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
     L.work_kv = take((size_t)b.kvbar * 4);
   }
   L.index_end = off;
-  if (with_dl) L.dl = take((size_t)p->total_q * p->num_heads_q * 4);
+  if (with_dl) {
+    L.dl = take((size_t)p->total_q * p->num_heads_q * 4);
+    L.lse2 = take((size_t)p->total_q * p->num_heads_q * 4);
+  }
   L.total = off;
   return L;
 }
@@ -417,7 +420,8 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   if (e != hipSuccess) return BSA_ERR_RUNTIME;
 
   float* dl = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.dl);
-  BwdPreArgs pa{out, dout, dl, p->total_q * p->num_heads_q};
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse2);
+  BwdPreArgs pa{out, dout, lse, dl, lse2, p->total_q * p->num_heads_q};
   prof_begin(BSA_KERNEL_BWD_PRE, s);
   e = launch_bwd_pre(pa, p->dtype, p->head_dim, s);
   prof_end(BSA_KERNEL_BWD_PRE, s);
@@ -429,6 +433,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.v = v;
   a.dout = dout;
   a.lse = lse;
+  a.lse2 = lse2;
   a.dl = dl;
   a.dq = dq;
   a.dk = dk;

@@ -13,6 +13,8 @@
 // the tile (the transposed, per-KV-block index lists).  dQ is a separate
 // Q-block-major pass over the forward's per-q-block lists, so no output is
 // accumulated with atomics and results are deterministic run to run.
+#include <type_traits>
+
 #include "bsa_attn.h"
 
 namespace bsa {
@@ -37,7 +39,10 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
   }
 #pragma unroll
   for (int m = CH / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < a.rows && c == 0) a.dl[row] = acc;
+  if (row < a.rows && c == 0) {
+    a.dl[row] = acc;
+    a.lse2[row] = a.lse[row] * LOG2E;
+  }
 }
 
 // -------------------------------------------------------------------- dQ --
@@ -45,10 +50,10 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 //   S^T = K Q^T, dP^T = V dO^T            (K, V row-major from LDS)
 //   P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T o (dP^T - D)
 //   dQ^T += K^T dS^T                       (K^T via LDS transpose loads)
-constexpr int DQ_STAGES = 4;  // LDS ring depth: K/V sub-tiles loaded 3 ahead
+constexpr int DQ_STAGES = 2;  // LDS ring depth (2 workgroups per CU share the LDS)
 
 template <typename MF, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   using L = XorTile<D>;  // K: read row-major (S^T) and transposed (dQ^T); V: row-major (dP^T)
   constexpr int TILE = L::template bytes<KT>();
   constexpr int STAGE = 2 * TILE;
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     dma.issue(st, qp + off, qstride, nvalid);
     dma.issue(st + TILE, dop + off, qstride, nvalid);
     float* stat = reinterpret_cast<float*>(st + 2 * TILE);
-    if (wv == 0) dma_rows_f32(stat, a.lse + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    if (wv == 0) dma_rows_f32(stat, a.lse2 + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     if (wv == 1) dma_rows_f32(stat + QS, a.dl + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     ld.next();
   };
@@ -339,47 +344,73 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
     const float* dll = lsel + QS;
 
-    const bool tail = nrows < QS;
+    // Rows past the sequence end, or keys above some row's causal limit,
+    // need masks; every other tile takes the mask-free path.
+    const bool masked = nrows < QS || (CAUSAL && key_lo + 127 > r0 + qoff);
+    {
+      // S, dP of query rows 32 h .. 32 h + 31 (operands read 4 MFMAs ahead)
+      auto sdp_pipelined = [&](int h, f32x16_t& s, f32x16_t& dp) {
+        mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * h, i >> 1); },
+                                  [&](int i, const u32x4_t& op) {
+                                    if (i & 1)
+                                      dp = MF::mfma(op, vf[i >> 1], dp);
+                                    else
+                                      s = MF::mfma(op, kf[i >> 1], s);
+                                  });
+      };
+      // P = exp(S scale - lse), dS = P o (dP - D), packed as MFMA operands
+      auto softmax = [&](int h, f32x16_t& s, f32x16_t& dp, u32x4_t& p0, u32x4_t& p1, u32x4_t& d0, u32x4_t& d1) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {  // 32-row halves of the q sub-tile
-      // S[qrow, key], dP[qrow, key] for query rows 32 t .. 32 t + 31
-      f32x16_t s = zero16(), dp = zero16();
-      // step i: kk = i / 2; even = S (Q rows), odd = dP (dO rows)
-      mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * t, i >> 1); },
-                                [&](int i, const u32x4_t& op) {
-                                  if (i & 1)
-                                    dp = MF::mfma(op, vf[i >> 1], dp);
-                                  else
-                                    s = MF::mfma(op, kf[i >> 1], s);
-                                });
+        for (int ig = 0; ig < 4; ++ig) {
+          const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
+          const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(lsel + rl);
+          const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(dll + rl);
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const int rl = 32 * t + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
-        const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(lsel + rl);
-        const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(dll + rl);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * ig + j;
-          float p = fast_exp2(fmaf(s[i], c2, -__uint_as_float(l4[j]) * LOG2E));
-          if (CAUSAL && my_key > r0 + rl + j + qoff) p = 0.f;
-          if (tail && rl + j >= nrows) p = 0.f;
-          s[i] = p;
-          dp[i] = p * (dp[i] - __uint_as_float(d4[j]));
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * ig + j;
+            const float p = fast_exp2(fmaf(s[i], c2, -__uint_as_float(l4[j])));
+            s[i] = p;
+            dp[i] = p * (dp[i] - __uint_as_float(d4[j]));
+          }
         }
+        if (masked) {  // edge tiles only: P = dS = 0 past the sequence end or the causal limit
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if ((CAUSAL && my_key > r0 + rl + qoff) || rl >= nrows) {
+              s[i] = 0.f;
+              dp[i] = 0.f;
+            }
+          }
+        }
+        p0 = pack8<MF>(s, 0);
+        p1 = pack8<MF>(s, 8);
+        d0 = pack8<MF>(dp, 0);
+        d1 = pack8<MF>(dp, 8);
+      };
+      // dV^T += dO^T P, dK^T += Q^T dS for query rows 32 h .. (chunks kc = 2 h, 2 h + 1)
+      auto dvdk_pipelined = [&](int h, const u32x4_t& p0, const u32x4_t& p1, const u32x4_t& d0,
+                                const u32x4_t& d1) {
+        mfma_pipeline<4 * NMT, 4>(
+            [&](int i) { return read_tr_operand((i & 1) ? ql : dl_, of, 16 * (2 * h + i / (2 * NMT)), (i >> 1) % NMT); },
+            [&](int i, const u32x4_t& op) {
+              const bool lo = i < 2 * NMT;
+              const int mt = (i >> 1) % NMT;
+              if (i & 1)
+                dk[mt] = MF::mfma(op, lo ? d0 : d1, dk[mt]);
+              else
+                dv[mt] = MF::mfma(op, lo ? p0 : p1, dv[mt]);
+            });
+      };
+
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // 32-row halves of the q sub-tile
+        f32x16_t s = zero16(), dp = zero16();
+        u32x4_t p0, p1, d0, d1;
+        sdp_pipelined(h, s, dp);
+        softmax(h, s, dp, p0, p1, d0, d1);
+        dvdk_pipelined(h, p0, p1, d0, d1);
       }
-      const u32x4_t pb0 = pack8<MF>(s, 0), pb1 = pack8<MF>(s, 8);
-      const u32x4_t sb0 = pack8<MF>(dp, 0), sb1 = pack8<MF>(dp, 8);
-      // step i: kc = 2 t + i / (2 NMT), mt = (i / 2) % NMT; even = dV^T, odd = dK^T
-      mfma_pipeline<4 * NMT, 4>(
-          [&](int i) { return read_tr_operand((i & 1) ? ql : dl_, of, 16 * (2 * t + i / (2 * NMT)), (i >> 1) % NMT); },
-          [&](int i, const u32x4_t& op) {
-            const bool lo = i < 2 * NMT;
-            const int mt = (i >> 1) % NMT;
-            if (i & 1)
-              dk[mt] = MF::mfma(op, lo ? sb0 : sb1, dk[mt]);
-            else
-              dv[mt] = MF::mfma(op, lo ? pb0 : pb1, dv[mt]);
-          });
     }
     stage = (stage + 1) % DKDV_STAGES;
   }
