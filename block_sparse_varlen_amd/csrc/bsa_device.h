@@ -154,6 +154,29 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Combines x of lane l and lane l ^ 32 with v_permlane32_swap (a VALU op, no
+// LDS round trip).  permlane32_swap(x, x) returns r0 = {x[0..31], x[0..31]}
+// and r1 = {x[32..63], x[32..63]} (checked on the hardware), so every lane
+// holds its own and its partner's value in r0 / r1.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Maximum of the 32 values of two accumulator fragments as a balanced tree.
+__device__ __forceinline__ float max32(const f32x16_t& a, const f32x16_t& b) {
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = fmaxf(fmaxf(a[4 * i], a[4 * i + 1]), fmaxf(a[4 * i + 2], a[4 * i + 3]));
+    m[4 + i] = fmaxf(fmaxf(b[4 * i], b[4 * i + 1]), fmaxf(b[4 * i + 2], b[4 * i + 3]));
+  }
+  return fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+}
+
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);

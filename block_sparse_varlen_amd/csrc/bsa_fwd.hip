@@ -37,19 +37,21 @@ constexpr float RESCALE_LOG2 = 8.f;
 
 template <typename MF, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
-  // K is read row-major only, V transposed only: each gets the padded layout
-  // that keeps its one read pattern free of bank conflicts.
-  using KL = PadTile<D, 16>;
+  // K is read row-major only (XOR-permuted chunks), V transposed only (rows
+  // padded by 64 bytes): both layouts keep their read pattern conflict free
+  // and both split into whole direct-to-LDS load instructions per wave.
+  using KL = XorTile<D>;
   using VL = PadTile<D, 64>;
   constexpr int KTILE = KL::template bytes<KT>();
   constexpr int VTILE = VL::template bytes<KT>();
-  constexpr int BUF = KTILE + VTILE;
+  constexpr int STAGE = KTILE + VTILE;
   constexpr int NMT = D / 32;  // 32-row feature tiles of O^T
   constexpr int NKK = D / 16;  // contraction steps over D
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   QItem it;
-  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it)) return;
+  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
+    return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int my_local = wv * 32 + (lane & 31);  // row within the item
   const int my_row = it.row_lo + my_local;     // row within the sequence
@@ -77,45 +79,47 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   const float c2 = a.sigma_log2e;
   const float thresh = RESCALE_LOG2 / c2;
 
-  Stage<KL, D, KT> sk;
-  Stage<VL, D, KT> sv;
-  sk.init(a.n2 * D);
-  sv.init(a.n2 * D);
-  SubTileWalk wk;
-  wk.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
-  auto load = [&](int key0) {
-    const int64_t off = kv_tile_offset<PAGED>(a.seq, a.block_table, it.b, it.g, key0, a.n2, D, a.page_size,
-                                              a.max_pages, a.page_stride);
-    const int nvalid = it.skv - key0;
-    sk.load(kbase_p + off, nvalid);
-    sv.load(vbase_p + off, nvalid);
-  };
+  DmaTile<KL, D, KT> kdma;
+  DmaTile<VL, D, KT> vdma;
+  kdma.init();
+  vdma.init();
   Operands<KL, D> ofk;
   Operands<VL, D> ofv;
   ofk.init();
   ofv.init();
-  // One 64-key sub-tile computed from LDS buffer `buf` (0/1).
-  auto step = [&](int buf) {
-    char* kl = smem + buf * BUF;
-    char* vl = kl + KTILE;
-    const int key0 = wk.key();
-    sk.store(kl);
-    sv.store(vl);
-    __syncthreads();
-    wk.next();
-    if (wk.valid()) load(wk.key());
+  // `ld` loads the sub-tile after the one `cp` computes (LDS double buffer)
+  SubTileWalk ld, cp;
+  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
+  cp = ld;
+  const int64_t kvrow = (int64_t)a.n2 * D;
+  auto issue = [&](int stage) {
+    char* st = smem + stage * STAGE;
+    const int key0 = ld.key();
+    const int64_t off = kv_tile_offset<PAGED>(a.seq, a.block_table, it.b, it.g, key0, a.n2, D, a.page_size,
+                                              a.max_pages, a.page_stride);
+    kdma.issue(st, kbase_p + off, kvrow, it.skv - key0);
+    vdma.issue(st + KTILE, vbase_p + off, kvrow, it.skv - key0);
+    ld.next();
+  };
+  if (ld.valid()) issue(0);
+  int stage = 0;
+  while (cp.valid()) {
+    wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
+    __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
+    if (ld.valid()) issue(stage ^ 1);
+    const int key0 = cp.key();
+    cp.next();
+    settle_scalar_loads();
+    const char* kl = smem + stage * STAGE;
+    const char* vl = kl + KTILE;
 
     // ---- S^T = K Q^T for keys key0 .. key0+63 (two 32-key tiles) ----
     f32x16_t s[2];
     s[0] = zero16();
     s[1] = zero16();
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4_t a0 = read_operand(kl, ofk, 0, kk);
-      const u32x4_t a1 = read_operand(kl, ofk, 32, kk);
-      s[0] = MF::mfma(a0, qf[kk], s[0]);
-      s[1] = MF::mfma(a1, qf[kk], s[1]);
-    }
+    // step i: kk = i / 2, key tile t = i % 2
+    mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand(kl, ofk, 32 * (i & 1), i >> 1); },
+                              [&](int i, const u32x4_t& op) { s[i & 1] = MF::mfma(op, qf[i >> 1], s[i & 1]); });
     // ---- masks: keys past Skv, causal limit (edge sub-tiles only) ----
     const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
     if (edge) {
@@ -129,12 +133,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
         }
     }
     // ---- online softmax (row = this lane's column) ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, wave_xor32(mx));
+    const float mx = half_max(max32(s[0], s[1]));
     // move the reference maximum only when it is exceeded by more than the threshold
     const bool upd = mx > m_run + thresh || (m_run == -INFINITY && mx > -INFINITY);
     if (__builtin_amdgcn_ballot_w64(upd)) {
@@ -148,36 +147,30 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run * c2;
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums (short dependency chains)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(s[t][i], c2, -m_use));
         s[t][i] = p;
-        psum += p;
+        ps[i & 3] += p;
       }
-    l_run += psum;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // ---- O^T += V^T P^T ----
     u32x4_t pb[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) pb[kc] = pack8<MF>(s[kc >> 1], 8 * (kc & 1));
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) o[mt] = MF::mfma(read_tr_operand(vl, ofv, 16 * kc, mt), pb[kc], o[mt]);
-  };
-  if (wk.valid()) load(wk.key());
-  int buf = 0;
-  while (wk.valid()) {
-    step(buf);
-    buf ^= 1;
+    // step i: kc = i / NMT, mt = i % NMT
+    mfma_pipeline<4 * NMT, 4>([&](int i) { return read_tr_operand(vl, ofv, 16 * (i / NMT), i % NMT); },
+                              [&](int i, const u32x4_t& op) { o[i % NMT] = MF::mfma(op, pb[i / NMT], o[i % NMT]); });
+    stage ^= 1;
   }
 
   // ---- epilogue: O = O^T / l, lse = scale * m + ln l ----
   // The two half-waves share m_run (the maximum is exchanged before use), so
   // their partial sums add directly.
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = half_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (it.q0 + my_row) * qstride + (int64_t)it.h * D;
