@@ -105,6 +105,40 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (N & 0xF) | ((N >> 4) << 14));
 }
 
+// One wave-wide global -> LDS copy: lane l fetches SIZE (4 or 16) bytes from
+// gbase + off (gbase wave-uniform, off the lane's byte offset) and they land
+// at LDS byte lds + SIZE l.  Issued as inline asm on purpose: when the
+// compiler sees a load that writes LDS it treats it as an access to two
+// memory kinds whose completion order it cannot track, and from then on waits
+// for every outstanding vector-memory and LDS operation (vmcnt(0) /
+// lgkmcnt(0)) before any LDS read -- which would drain the next stage's
+// prefetch in the middle of the current stage.  The kernels synchronise these
+// copies themselves: wait_vmcnt for the issuing wave, then a workgroup
+// barrier before any wave reads the stage.  M0 holds the LDS base (no other
+// code in these kernels uses M0); one wait state separates its write from the
+// copy.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(const void* gbase, uint32_t off, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(lds));
+  const uint64_t gb = (uint64_t)(uintptr_t)gbase;
+  // readfirstlane returns int: take each half as unsigned before widening
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gb);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (SIZE == 16) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0)
+                 : "memory", "m0");
+  } else {
+    static_assert(SIZE == 4, "4- or 16-byte copies");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sb), "s"(m0)
+                 : "memory", "m0");
+  }
+#pragma clang diagnostic pop
+}
+
 // Direct global -> LDS staging (global_load_lds_dwordx4) of a ROWS x D tile
 // with layout L.  Lane l of a wave instruction writes LDS bytes base + 16 l
 // (checked on the hardware), so instruction i fills 16-byte slots
@@ -137,16 +171,45 @@ struct DmaTile {
       col[j] = 8 * chunk;
     }
   }
-  // gbase: element pointer of tile row 0, column 0; rows are row_stride apart
-  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int64_t row_stride, int nvalid) const {
+  // gbase: element pointer of tile row 0, column 0 (wave-uniform); rows are
+  // row_stride elements apart
+  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int row_stride, int nvalid) const {
     const int wv = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int r = min(row[j], nvalid - 1);
-      const uint16_t* src = gbase + r * row_stride + col[j];
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)(lds_tile + 1024 * (wv + 4 * j)), 16,
-                                       0, 0);
+      dma_to_lds<16>(gbase, 2u * (uint32_t)(r * row_stride + col[j]), lds_tile + 1024 * (wv + 4 * j));
+    }
+  }
+};
+
+// The same direct staging for an XorTile<D> of ROWS rows by a workgroup of NW
+// waves.  Wave w's instruction j fills slots 64 (w + NW j) .. + 63, i.e. rows
+// r0 + RSTEP j of the lane; the XOR pattern repeats every PERIOD instructions,
+// so only the row of j = 0 and PERIOD column offsets are kept per lane.
+template <int D, int ROWS, int NW>
+struct DmaXor {
+  using L = XorTile<D>;
+  static constexpr int SPR = D / 8;
+  static constexpr int NINST = ROWS * SPR / 64;
+  static constexpr int PER_WAVE = NINST / NW;
+  static constexpr int RSTEP = 64 * NW / SPR;
+  static constexpr int PERIOD = RSTEP % 16 == 0 ? 1 : RSTEP % 8 == 0 ? 2 : RSTEP % 4 == 0 ? 4 : 16;
+  static_assert(64 % SPR == 0 && NINST % NW == 0, "tile must split evenly over the waves");
+  int r0;
+  int col[PERIOD];
+  __device__ __forceinline__ void init() {
+    const int wv = threadIdx.x >> 6, lane = lane_id();
+    r0 = 64 * wv / SPR + lane / SPR;
+#pragma unroll
+    for (int p = 0; p < PERIOD; ++p) col[p] = 8 * ((lane % SPR) ^ L::swz(r0 + RSTEP * p));
+  }
+  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int row_stride, int nvalid) const {
+    const int wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int r = min(r0 + RSTEP * j, nvalid - 1);
+      dma_to_lds<16>(gbase, 2u * (uint32_t)(r * row_stride + col[j % PERIOD]), lds_tile + 1024 * (wv + NW * j));
     }
   }
 };
@@ -162,10 +225,9 @@ __device__ __forceinline__ void settle_scalar_loads() {
 
 // One fp32 per row of a 64-row tile, loaded by one wave into LDS (lane l ->
 // bytes 4 l); rows at or past nvalid repeat row nvalid - 1.
-__device__ __forceinline__ void dma_rows_f32(float* lds, const float* g, int64_t stride, int nvalid) {
+__device__ __forceinline__ void dma_rows_f32(float* lds, const float* g, int stride, int nvalid) {
   const int r = min(lane_id(), nvalid - 1);
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(g + r * stride),
-                                   (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
+  dma_to_lds<4>(g, 4u * (uint32_t)(r * stride), lds);
 }
 
 // Element offset of key `key0` (row 0 of a sub-tile that stays inside one
@@ -293,6 +355,7 @@ __device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, const Operan
 template <int N, int LOOK, class ReadF, class MfmaF>
 __device__ __forceinline__ void mfma_pipeline(ReadF read, MfmaF mfma) {
   u32x4_t ring[LOOK];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < LOOK; ++i) ring[i] = read(i);
 #pragma unroll

@@ -50,7 +50,6 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 //   S^T = K Q^T, dP^T = V dO^T            (K, V row-major from LDS)
 //   P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T o (dP^T - D)
 //   dQ^T += K^T dS^T                       (K^T via LDS transpose loads)
-constexpr int DQ_STAGES = 2;  // LDS ring depth (2 workgroups per CU share the LDS)
 
 template <typename MF, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
@@ -60,13 +59,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   constexpr int NMT = D / 32;
   constexpr int NKK = D / 16;
   using Dma = DmaTile<L, D, KT>;
-  constexpr int OPS = 2 * Dma::PER_WAVE;  // vector-memory operations per staged sub-tile and wave
-  __shared__ __attribute__((aligned(16))) char smem[DQ_STAGES * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];  // double buffer
 
   QItem it;
   if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
     return;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int my_local = wv * 32 + (lane & 31);
   const int my_row = it.row_lo + my_local;
   const bool row_ok = my_local < it.nrows;
@@ -98,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   dma.init();
   Operands<L, D> of;
   of.init();
-  // `ld` issues sub-tile loads DQ_STAGES - 1 ahead of `cp`, which computes
+  // `ld` loads the sub-tile after the one `cp` computes (LDS double buffer)
   SubTileWalk ld, cp;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
   cp = ld;
@@ -106,23 +104,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.key();
     const int64_t off = kv_tile_offset<false>(a.seq, nullptr, it.b, it.g, key0, a.n2, D, 0, 0, 0);
-    dma.issue(st, kp + off, (int64_t)a.n2 * D, it.skv - key0);
-    dma.issue(st + TILE, vp + off, (int64_t)a.n2 * D, it.skv - key0);
+    dma.issue(st, kp + off, a.n2 * D, it.skv - key0);
+    dma.issue(st + TILE, vp + off, a.n2 * D, it.skv - key0);
     ld.next();
   };
-  int nld = 0;
-  while (ld.valid() && nld < DQ_STAGES - 1) issue(nld++);
-  int ahead = nld - 1;
+  if (ld.valid()) issue(0);
   int stage = 0;
   while (cp.valid()) {
-    if (ahead >= 2) wait_vmcnt<2 * OPS>();
-    else if (ahead == 1) wait_vmcnt<OPS>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's loads landed; the stage reloaded below is free
-    if (ld.valid())
-      issue((stage + DQ_STAGES - 1) % DQ_STAGES);
-    else
-      --ahead;
+    wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
+    __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
+    if (ld.valid()) issue(stage ^ 1);
     const int key0 = cp.key();
     cp.next();
     settle_scalar_loads();
@@ -152,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
           [&](int i) { return read_tr_operand(kl, of, 16 * (2 * t + i / NMT), i % NMT); },
           [&](int i, const u32x4_t& op) { acc[i % NMT] = MF::mfma(op, (i < NMT) ? db0 : db1, acc[i % NMT]); });
     }
-    stage = (stage + 1) % DQ_STAGES;
+    stage ^= 1;
   }
   if (row_ok) {
     uint16_t* op = reinterpret_cast<uint16_t*>(a.dq) + tok * qstride + (int64_t)it.h * D;
@@ -216,20 +207,17 @@ struct ColWalk {
   __device__ __forceinline__ int row0() const { return ldu(qrows, e) * 128 + half * QS; }
 };
 
-constexpr int DKDV_STAGES = 4;  // LDS ring depth: Q/dO tiles loaded 3 sub-tiles ahead
+constexpr int DKDV_WAVES = 2;   // a workgroup's waves, 64 keys each
+constexpr int DKDV_STAGES = 2;  // LDS ring depth (two workgroups per CU share the LDS)
 
 template <typename MF, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   using QL = XorTile<D>;  // Q and dO: read row-major (S, dP) and transposed (dK^T, dV^T)
   constexpr int TILE = QL::template bytes<QS>();
   constexpr int STAGE = 2 * TILE + 2 * QS * 4;  // Q, dO, lse, D
   constexpr int NMT = D / 32;
   constexpr int NKK = D / 16;
-  using Dma = DmaTile<QL, D, QS>;
-  // vector-memory operations per staged tile for this wave: Q and dO chunks,
-  // plus the lse row (wave 0) or the D row (wave 1)
-  constexpr int OPS_LO = 2 * Dma::PER_WAVE + 1;  // waves 0, 1
-  constexpr int OPS_HI = 2 * Dma::PER_WAVE;      // waves 2, 3
+  using Dma = DmaXor<D, QS, DKDV_WAVES>;
   __shared__ __attribute__((aligned(16))) char smem[DKDV_STAGES * STAGE];
 
   const int KVI = ldu(a.hdr, H_KVITEMS);
@@ -248,31 +236,37 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
   const int skv = (int)(ldu(a.seq.cu_kv, b + 1) - kv0);
   const int key_lo = kb * a.seq.by + sub * 128;
   if (key_lo >= skv) return;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int my_key = key_lo + wv * 32 + (lane & 31);
-  const bool key_ok = my_key < skv;
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // this lane's keys: column lane % 32 of the wave's two 32-key tiles
+  const int key_w = key_lo + 64 * wv + (lane & 31);
   const int qoff = skv - sq;
   const int64_t kvstride = (int64_t)a.n2 * D;
-  const int64_t krow = (kv0 + my_key) * kvstride + (int64_t)g * D + 8 * (lane >> 5);
-  u32x4_t kf[NKK], vf[NKK];
+  u32x4_t kf[2][NKK], vf[2][NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    kf[kk] = key_ok ? gload16(reinterpret_cast<const uint16_t*>(a.k) + krow + 16 * kk) : zero_u4();
-    vf[kk] = key_ok ? gload16(reinterpret_cast<const uint16_t*>(a.v) + krow + 16 * kk) : zero_u4();
-  }
-  f32x16_t dk[NMT], dv[NMT];
+  for (int n = 0; n < 2; ++n) {
+    const int key = key_w + 32 * n;
+    const int64_t krow = (kv0 + key) * kvstride + (int64_t)g * D + 8 * (lane >> 5);
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
-    dk[mt] = zero16();
-    dv[mt] = zero16();
+    for (int kk = 0; kk < NKK; ++kk) {
+      kf[n][kk] = key < skv ? gload16(reinterpret_cast<const uint16_t*>(a.k) + krow + 16 * kk) : zero_u4();
+      vf[n][kk] = key < skv ? gload16(reinterpret_cast<const uint16_t*>(a.v) + krow + 16 * kk) : zero_u4();
+    }
   }
+  f32x16_t dk[2][NMT], dv[2][NMT];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      dk[n][mt] = zero16();
+      dv[n][mt] = zero16();
+    }
   const float c2 = a.sigma_log2e;
-  const int64_t qstride = (int64_t)a.n1 * D;
+  const int qstride = a.n1 * D;
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* dop = reinterpret_cast<const uint16_t*>(a.dout);
 
   // Two cursors over the same (head, q-block, half) sequence: `ld` issues the
-  // loads DKDV_STAGES - 1 tiles ahead of `cp`, which computes.
+  // loads of the next tile while `cp` computes the current one.
   ColWalk ld, cp;
   ld.col_ptr = a.col_ptr;
   ld.qrows = a.qrows;
@@ -300,41 +294,21 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     const int h = g * a.group + ld.hh;
     const int r0 = ld.row0();
     const int nvalid = sq - r0;
-    const int64_t off = (q0 + r0) * qstride + (int64_t)h * D;
+    const int64_t off = (q0 + r0) * (int64_t)qstride + (int64_t)h * D;
     dma.issue(st, qp + off, qstride, nvalid);
     dma.issue(st + TILE, dop + off, qstride, nvalid);
     float* stat = reinterpret_cast<float*>(st + 2 * TILE);
-    if (wv == 0) dma_rows_f32(stat, a.lse2 + (q0 + r0) * a.n1 + h, a.n1, nvalid);
-    if (wv == 1) dma_rows_f32(stat + QS, a.dl + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    // lse (wave 0) and D (wave 1) of the tile's rows
+    dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.dl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     ld.next();
   };
 
-  int ahead = 0;  // tiles issued beyond the one being computed
-  int stage_ld = 0;
-  while (ld.valid() && stage_ld < DKDV_STAGES - 1) {
-    issue(stage_ld);
-    ++stage_ld;
-  }
-  ahead = stage_ld - 1;
+  if (ld.valid()) issue(0);
   int stage = 0;
   while (cp.valid()) {
-    // this wave's loads for the current tile are done once at most `ahead`
-    // tiles' worth of its operations are still in flight
-    if (wv < 2) {
-      if (ahead >= 2) wait_vmcnt<2 * OPS_LO>();
-      else if (ahead == 1) wait_vmcnt<OPS_LO>();
-      else wait_vmcnt<0>();
-    } else {
-      if (ahead >= 2) wait_vmcnt<2 * OPS_HI>();
-      else if (ahead == 1) wait_vmcnt<OPS_HI>();
-      else wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();  // every wave's loads landed; the stage freed below is no longer read
-    if (ld.valid()) {
-      issue((stage + DKDV_STAGES - 1) % DKDV_STAGES);
-    } else {
-      --ahead;
-    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // both waves' loads landed; the other stage is no longer read
+    if (ld.valid()) issue(stage ^ 1);
     const int r0 = cp.row0();
     const int nrows = sq - r0;  // valid rows of this tile (may exceed QS)
     cp.next();
@@ -347,81 +321,97 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     // Rows past the sequence end, or keys above some row's causal limit,
     // need masks; every other tile takes the mask-free path.
     const bool masked = nrows < QS || (CAUSAL && key_lo + 127 > r0 + qoff);
-    {
-      // S, dP of query rows 32 h .. 32 h + 31 (operands read 4 MFMAs ahead)
-      auto sdp_pipelined = [&](int h, f32x16_t& s, f32x16_t& dp) {
-        mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * h, i >> 1); },
-                                  [&](int i, const u32x4_t& op) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        s[n] = zero16();
+        dp[n] = zero16();
+      }
+      // S, dP of rows 32 h .. + 31: each Q / dO operand read feeds both key tiles
+      mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * h, i >> 1); },
+                                [&](int i, const u32x4_t& op) {
+#pragma unroll
+                                  for (int n = 0; n < 2; ++n) {
                                     if (i & 1)
-                                      dp = MF::mfma(op, vf[i >> 1], dp);
+                                      dp[n] = MF::mfma(op, vf[n][i >> 1], dp[n]);
                                     else
-                                      s = MF::mfma(op, kf[i >> 1], s);
-                                  });
-      };
-      // P = exp(S scale - lse), dS = P o (dP - D), packed as MFMA operands
-      auto softmax = [&](int h, f32x16_t& s, f32x16_t& dp, u32x4_t& p0, u32x4_t& p1, u32x4_t& d0, u32x4_t& d1) {
+                                      s[n] = MF::mfma(op, kf[n][i >> 1], s[n]);
+                                  }
+                                });
+      // P = exp2(S scale log2e - lse log2e), dS = P o (dP - D)
+      u32x4_t pb[2][2], db[2][2];
 #pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
-          const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(lsel + rl);
-          const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(dll + rl);
+      for (int ig = 0; ig < 4; ++ig) {
+        const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
+        const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(lsel + rl);
+        const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(dll + rl);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * ig + j;
-            const float p = fast_exp2(fmaf(s[i], c2, -__uint_as_float(l4[j])));
-            s[i] = p;
-            dp[i] = p * (dp[i] - __uint_as_float(d4[j]));
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * ig + j;
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const float p = fast_exp2(fmaf(s[n][i], c2, -__uint_as_float(l4[j])));
+            s[n][i] = p;
+            dp[n][i] = p * (dp[n][i] - __uint_as_float(d4[j]));
           }
         }
-        if (masked) {  // edge tiles only: P = dS = 0 past the sequence end or the causal limit
+      }
+      if (masked) {  // edge tiles only: P = dS = 0 past the sequence end or the causal limit
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if ((CAUSAL && my_key > r0 + rl + qoff) || rl >= nrows) {
-              s[i] = 0.f;
-              dp[i] = 0.f;
+        for (int i = 0; i < 16; ++i) {
+          const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            if ((CAUSAL && key_w + 32 * n > r0 + rl + qoff) || rl >= nrows) {
+              s[n][i] = 0.f;
+              dp[n][i] = 0.f;
             }
           }
         }
-        p0 = pack8<MF>(s, 0);
-        p1 = pack8<MF>(s, 8);
-        d0 = pack8<MF>(dp, 0);
-        d1 = pack8<MF>(dp, 8);
-      };
-      // dV^T += dO^T P, dK^T += Q^T dS for query rows 32 h .. (chunks kc = 2 h, 2 h + 1)
-      auto dvdk_pipelined = [&](int h, const u32x4_t& p0, const u32x4_t& p1, const u32x4_t& d0,
-                                const u32x4_t& d1) {
-        mfma_pipeline<4 * NMT, 4>(
-            [&](int i) { return read_tr_operand((i & 1) ? ql : dl_, of, 16 * (2 * h + i / (2 * NMT)), (i >> 1) % NMT); },
-            [&](int i, const u32x4_t& op) {
-              const bool lo = i < 2 * NMT;
-              const int mt = (i >> 1) % NMT;
-              if (i & 1)
-                dk[mt] = MF::mfma(op, lo ? d0 : d1, dk[mt]);
-              else
-                dv[mt] = MF::mfma(op, lo ? p0 : p1, dv[mt]);
-            });
-      };
-
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {  // 32-row halves of the q sub-tile
-        f32x16_t s = zero16(), dp = zero16();
-        u32x4_t p0, p1, d0, d1;
-        sdp_pipelined(h, s, dp);
-        softmax(h, s, dp, p0, p1, d0, d1);
-        dvdk_pipelined(h, p0, p1, d0, d1);
       }
-    }
-    stage = (stage + 1) % DKDV_STAGES;
-  }
-  if (key_ok) {
-    const int64_t orow = (kv0 + my_key) * kvstride + (int64_t)g * D;
-    uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + orow;
-    uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + orow;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      store_cols<MF>(dkp, 32 * mt, dk[mt], a.sigma);
-      store_cols<MF>(dvp, 32 * mt, dv[mt], 1.f);
+      for (int n = 0; n < 2; ++n) {
+        pb[n][0] = pack8<MF>(s[n], 0);
+        pb[n][1] = pack8<MF>(s[n], 8);
+        db[n][0] = pack8<MF>(dp[n], 0);
+        db[n][1] = pack8<MF>(dp[n], 8);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS over the 16-row chunks 2 h, 2 h + 1;
+      // each transposed operand read feeds both key tiles
+      mfma_pipeline<4 * NMT, 4>(
+          [&](int i) { return read_tr_operand((i & 1) ? ql : dl_, of, 16 * (2 * h + i / (2 * NMT)), (i >> 1) % NMT); },
+          [&](int i, const u32x4_t& op) {
+            const int c = i / (2 * NMT);
+            const int mt = (i >> 1) % NMT;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              if (i & 1)
+                MF::mfma_acc(dk[n][mt], op, db[n][c]);
+              else
+                MF::mfma_acc(dv[n][mt], op, pb[n][c]);
+            }
+          });
+    }
+    stage ^= 1;
+  }
+  mfma_acc_done(dk[0]);
+  mfma_acc_done(dk[1]);
+  mfma_acc_done(dv[0]);
+  mfma_acc_done(dv[1]);
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int key = key_w + 32 * n;
+    if (key < skv) {
+      const int64_t orow = (kv0 + key) * kvstride + (int64_t)g * D;
+      uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + orow;
+      uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + orow;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        store_cols<MF>(dkp, 32 * mt, dk[n][mt], a.sigma);
+        store_cols<MF>(dvp, 32 * mt, dv[n][mt], 1.f);
+      }
     }
   }
 }
@@ -437,9 +427,9 @@ hipError_t launch_dq_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
 template <typename MF, int D>
 hipError_t launch_dkdv_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
   if (a.seq.causal)
-    k_bwd_dkdv<MF, D, true><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_bwd_dkdv<MF, D, true><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
   else
-    k_bwd_dkdv<MF, D, false><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_bwd_dkdv<MF, D, false><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
   return hipGetLastError();
 }
 

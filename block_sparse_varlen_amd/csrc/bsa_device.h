@@ -35,6 +35,10 @@ struct BF16 {
   static __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
   }
+  // acc += A B with acc held in accumulation registers (AGPRs); see mfma_acc_done.
+  static __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
   // Two fp32 values rounded to nearest-even bf16, packed lo | hi << 16.
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     bf16x2_t r;
@@ -51,6 +55,9 @@ struct F16 {
   static __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     f16x2_t r;
     r[0] = (_Float16)lo;
@@ -64,6 +71,21 @@ struct F16 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
   }
 };
+
+// mfma_acc pins a long-lived accumulator to the AGPRs, leaving the VGPRs to
+// the operands and to the MFMA results the softmax works on.  The compiler
+// cannot see that the asm is an MFMA, so two of its hazards are covered by
+// hand: the B operand is never written by the instruction just before (the
+// callers start a run of mfma_acc after LDS reads), and before the
+// accumulators are read back mfma_acc_done waits out the MFMA latency (XDL
+// result -> VALU read needs at most 19 wait states on CDNA3/4), tied to each
+// accumulator so that no read is scheduled ahead of it.
+template <int N>
+__device__ __forceinline__ void mfma_acc_done(f32x16_t (&acc)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
 
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;

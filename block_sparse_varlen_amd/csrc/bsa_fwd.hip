@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   SubTileWalk ld, cp;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
   cp = ld;
-  const int64_t kvrow = (int64_t)a.n2 * D;
+  const int kvrow = a.n2 * D;
   auto issue = [&](int stage) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.key();
