@@ -106,7 +106,58 @@ def cpu_baseline(case, budget_s: float):
                       f"{dt:.1f} s of fp64 NumPy (BLAS threads={threads})"}
 
 
+# bench kernel keys by the HIP kernel names rocprofv3 reports
+KERNEL_KEYS = {"k_fwd<": "fwd", "k_bwd_dkdv<": "bwd_dkdv", "k_bwd_dq<": "bwd_dq", "k_bwd_pre<": "bwd_pre"}
+CALIB_BYTES = 512 << 20  # --calib-copy: y = x * 1 over 512 MiB of fp32 (reads and writes that much)
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> None:
+    """Per-launch HBM bytes of each attention kernel from two rocprofv3 --pmc
+    runs of ``bench.py --calib-copy`` (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch).  Each counter is scaled by bytes / counter of the calibration
+    multiply, whose traffic is known.  Writes TRAFFIC_FILE, keyed by the hash
+    of each kernel's sources so that a later change of a kernel invalidates
+    its entry."""
+    import csv
+
+    def per_dispatch(path, counter):
+        tot, disp = {}, {}
+        calib = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "MulFunctor" in name:
+                calib.append(v)
+                continue
+            for pat, key in KERNEL_KEYS.items():
+                if pat in name:
+                    tot[key] = tot.get(key, 0.0) + v
+                    disp.setdefault(key, set()).add(r["Dispatch_Id"])
+        if not calib:
+            raise SystemExit(f"{path}: no calibration multiply found (run bench.py with --calib-copy)")
+        scale = CALIB_BYTES / (sum(calib) / len(calib) * 1024.0)
+        return {k: tot[k] / len(disp[k]) * 1024.0 * scale for k in tot}, scale
+
+    fetch, fs = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, ws = per_dispatch(write_csv, "WRITE_SIZE")
+    out = {"_note": "HBM bytes per launch = FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale (counters in KiB; "
+                    "scales from a 512 MiB copy)", "_fetch_scale": fs, "_write_scale": ws}
+    for k in sorted(set(fetch) & set(write)):
+        ent = {"fetch_bytes": round(fetch[k]), "write_bytes": round(write[k]),
+               "bytes_per_launch": round(fetch[k] + write[k])}
+        if k in KERNEL_SOURCES:
+            ent["source_sha"] = kernel_source_sha(k)
+        out[k] = ent
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--write-traffic":
+        write_traffic(sys.argv[2], sys.argv[3])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)

@@ -12,6 +12,14 @@ from __future__ import annotations
 import ctypes
 import os
 
+# PyTorch ships its own HIP runtime under the same soname (libamdhip64.so.7)
+# as the ROCm one libbsa.so links against, and the first library loaded
+# serves the whole process.  Loading torch first keeps a single runtime --
+# the one that owns the tensors and streams handed to the library; loading
+# libbsa.so first would bind torch to a runtime its bundled libraries were
+# not built with, and launches then fail.
+import torch  # noqa: F401  (runtime selection only)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsa.so")
 

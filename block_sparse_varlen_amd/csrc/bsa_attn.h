@@ -245,9 +245,11 @@ __device__ __forceinline__ int64_t kv_tile_offset(const SeqArgs& seq, const int3
   }
 }
 
-// Walk over the 64-key sub-tiles of a CSR row: blocks cols[e0..e1), each cut
-// into by / 64 sub-tiles, keeping those whose first key is below `kend` (the
-// key bound of the item: Skv, or the causal limit of its last row + 1).
+// Walk over the T-key sub-tiles of a CSR row: blocks cols[e0..e1), each cut
+// into by / T sub-tiles, keeping those whose first key is below `kend` (the
+// key bound of the item: Skv, or the causal limit of its last row + 1).  Every
+// listed block starts below kend, so only the later sub-tiles are tested.
+template <int T = KT>
 struct SubTileWalk {
   const int32_t* cols;
   int e, e1, s, nsub, by, kend;
@@ -257,14 +259,14 @@ struct SubTileWalk {
     e1 = e_end;
     s = 0;
     by = by_;
-    nsub = by_ / KT;
+    nsub = by_ / T;
     kend = kend_;
   }
   __device__ __forceinline__ bool valid() const { return e < e1; }
-  __device__ __forceinline__ int key() const { return ldu(cols, e) * by + s * KT; }
+  __device__ __forceinline__ int key() const { return ldu(cols, e) * by + s * T; }
   __device__ __forceinline__ void next() {
     ++s;
-    if (s >= nsub || ldu(cols, e) * by + s * KT >= kend) {
+    if (s >= nsub || ldu(cols, e) * by + s * T >= kend) {
       ++e;
       s = 0;
     }
@@ -365,6 +367,33 @@ __device__ __forceinline__ void mfma_pipeline(ReadF read, MfmaF mfma) {
     mfma(i, a);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// mfma_pipeline with a third callback: extra(i) emits work independent of the
+// pipeline (another tile's softmax) right after step i's MFMAs, so the VALU
+// issues while the matrix core is still busy with them.
+template <int N, int LOOK, class ReadF, class MfmaF, class ExtraF>
+__device__ __forceinline__ void mfma_pipeline_x(ReadF read, MfmaF mfma, ExtraF extra) {
+  u32x4_t ring[LOOK];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < LOOK; ++i) ring[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const u32x4_t a = ring[i % LOOK];
+    if (i + LOOK < N) ring[i % LOOK] = read(i + LOOK);
+    mfma(i, a);
+    extra(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Maximum of the 16 values of an accumulator fragment as a balanced tree.
+__device__ __forceinline__ float max16(const f32x16_t& a) {
+  float m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[i] = fmaxf(fmaxf(a[4 * i], a[4 * i + 1]), fmaxf(a[4 * i + 2], a[4 * i + 3]));
+  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
 }
 
 // Stores a [32 x 32] C fragment holding X^T (rows = feature d, columns =

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   Operands<L, D> of;
   of.init();
   // `ld` loads the sub-tile after the one `cp` computes (LDS double buffer)
-  SubTileWalk ld, cp;
+  SubTileWalk<> ld, cp;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
   cp = ld;
   auto issue = [&](int stage) {
@@ -153,15 +153,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- dK, dV --
-// Work item: one 128-key tile of KV block (g, b, kb); wave w owns keys
-// 32w .. 32w+31 and keeps its K and V rows in registers as the B operands of
-// S = Q K^T and dP = dO V^T.  For every q-head of the group and every q-block
-// in the tile's transposed list, 64-row query sub-tiles of Q, dO, lse and D
-// are staged through double-buffered LDS and each wave computes
+// Work item: one 128-key tile of KV block (g, b, kb), taken by a workgroup of
+// two waves; wave w owns keys 64 w .. 64 w + 63 as two 32-key tiles and keeps
+// their K and V rows in registers as the B operands of S = Q K^T and
+// dP = dO V^T.  For every q-head of the group and every q-block in the tile's
+// transposed list, 64-row query sub-tiles of Q, dO, lse and D are staged
+// through double-buffered LDS and each wave computes, per 32-row half,
 //   S, dP                (MFMA, Q / dO row-major from LDS)
 //   P = exp2(S scale log2e - lse log2e), dS = P o (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (Q^T / dO^T via LDS transpose loads,
 //                                      P / dS straight from registers)
+// Every operand read from LDS feeds the MFMAs of both key tiles; dK and dV
+// accumulate in AGPRs.
 constexpr int QS = 64;  // query rows per staged sub-tile
 
 // Walk over (q-head of the group, q-block of the tile's column list, 64-row

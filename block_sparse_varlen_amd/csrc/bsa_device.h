@@ -37,7 +37,15 @@ struct BF16 {
   }
   // acc += A B with acc held in accumulation registers (AGPRs); see mfma_acc_done.
   static __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+  // acc = A B (first) or acc += A B with the B operand held in AGPRs and acc in
+  // VGPRs; see mfma_vgpr_done.
+  static __device__ __forceinline__ void mfma_bagpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b, bool first) {
+    if (first)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+    else
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
   }
   // Two fp32 values rounded to nearest-even bf16, packed lo | hi << 16.
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
@@ -56,7 +64,13 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void mfma_bagpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b, bool first) {
+    if (first)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+    else
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
   }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     f16x2_t r;
@@ -72,19 +86,38 @@ struct F16 {
   }
 };
 
-// mfma_acc pins a long-lived accumulator to the AGPRs, leaving the VGPRs to
-// the operands and to the MFMA results the softmax works on.  The compiler
-// cannot see that the asm is an MFMA, so two of its hazards are covered by
-// hand: the B operand is never written by the instruction just before (the
-// callers start a run of mfma_acc after LDS reads), and before the
-// accumulators are read back mfma_acc_done waits out the MFMA latency (XDL
-// result -> VALU read needs at most 19 wait states on CDNA3/4), tied to each
-// accumulator so that no read is scheduled ahead of it.
+// mfma_acc pins a long-lived accumulator to the AGPRs, and mfma_bagpr a
+// long-lived B operand, leaving the VGPRs to the operands and to the MFMA
+// results the softmax works on.  The compiler cannot see that the asm is an
+// MFMA, so it inserts none of the MFMA wait states; two are covered by hand:
+//  * a VALU write of an operand register (the compiler may stage an operand
+//    through a copy right before the asm) needs 2 wait states before the
+//    MFMA reads it: each asm MFMA starts with s_nop 1, which issues while the
+//    matrix pipe is still busy with the previous MFMA;
+//  * before the results are read back, mfma_acc_done / mfma_vgpr_done wait
+//    out the MFMA latency (XDL result -> VALU read needs at most 19 wait
+//    states on CDNA3/4), tied to each accumulator so that no read is
+//    scheduled ahead of the wait.
 template <int N>
 __device__ __forceinline__ void mfma_acc_done(f32x16_t (&acc)[N]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]));
 #pragma unroll
   for (int i = 1; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
+// The same wait for VGPR results of mfma_bagpr before VALU code reads them.
+template <int N>
+__device__ __forceinline__ void mfma_vgpr_done(f32x16_t (&acc)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("" : "+v"(acc[i]));
+}
+
+// Pins the computation of x to this point of the instruction stream: the
+// compiler must have x in a VGPR here and may not sink its producers past it
+// (used to keep independent VALU work interleaved with MFMA runs).
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 __device__ __forceinline__ f32x16_t zero16() {

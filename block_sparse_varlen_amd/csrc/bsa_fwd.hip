@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   ofk.init();
   ofv.init();
   // `ld` loads the sub-tile after the one `cp` computes (LDS double buffer)
-  SubTileWalk ld, cp;
+  SubTileWalk<> ld, cp;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
   cp = ld;
   const int kvrow = a.n2 * D;
