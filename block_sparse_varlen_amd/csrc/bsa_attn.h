@@ -117,35 +117,50 @@ __device__ __forceinline__ void wait_vmcnt() {
 // barrier before any wave reads the stage.  M0 holds the LDS base (no other
 // code in these kernels uses M0); one wait state separates its write from the
 // copy.
+// LDS byte address of a pointer into __shared__ memory, and a 64-bit value
+// made wave-uniform (readfirstlane returns int: each half is taken as
+// unsigned before widening).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// The copy itself, from wave-uniform sbase (global byte address) and m0 (LDS
+// byte address) and the lane's byte offset voff.
 template <int SIZE>
-__device__ __forceinline__ void dma_to_lds(const void* gbase, uint32_t off, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(lds));
-  const uint64_t gb = (uint64_t)(uintptr_t)gbase;
-  // readfirstlane returns int: take each half as unsigned before widening
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gb);
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+__device__ __forceinline__ void dma_raw(uint64_t sbase, uint32_t voff, uint32_t m0) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   if constexpr (SIZE == 16) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
   } else {
     static_assert(SIZE == 4, "4- or 16-byte copies");
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sb), "s"(m0)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
   }
 #pragma clang diagnostic pop
 }
 
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(const void* gbase, uint32_t off, const void* lds) {
+  dma_raw<SIZE>(uniform_u64((uint64_t)(uintptr_t)gbase), off, __builtin_amdgcn_readfirstlane(lds_addr(lds)));
+}
+
 // Direct global -> LDS staging (global_load_lds_dwordx4) of a ROWS x D tile
-// with layout L.  Lane l of a wave instruction writes LDS bytes base + 16 l
-// (checked on the hardware), so instruction i fills 16-byte slots
-// 64 i .. 64 i + 63 of the tile; each lane fetches the global chunk that the
-// layout puts in its slot (pad slots fetch a harmless chunk).  The tile's
-// NINST instructions are spread over the 4 waves, PER_WAVE each.  Rows at or
-// past `nvalid` are fetched from row nvalid - 1 (finite data the kernel then
+// with layout L, rows row_stride elements apart in global memory.  Lane l of
+// a wave instruction writes LDS bytes base + 16 l (checked on the hardware),
+// so instruction i fills 16-byte slots 64 i .. 64 i + 63 of the tile; each
+// lane fetches the global chunk that the layout puts in its slot (pad slots
+// fetch a harmless chunk).  The tile's NINST instructions are spread over the
+// 4 waves, PER_WAVE each.  The lanes' byte offsets of a full tile are fixed
+// for a work item and kept in registers, so a copy costs no vector ALU work;
+// in a partial tile (rows at or past `nvalid`, the last tile of a sequence)
+// those rows are fetched from row nvalid - 1 (finite data the kernel then
 // masks), so no lane reads outside the tensor.
 template <class L, int D, int ROWS>
 struct DmaTile {
@@ -153,32 +168,44 @@ struct DmaTile {
   static constexpr int NINST = ROWS * SPR / 64;
   static constexpr int PER_WAVE = NINST / 4;
   static_assert((ROWS * SPR) % 64 == 0 && NINST % 4 == 0, "tile must split evenly over 4 waves");
-  int row[PER_WAVE];
-  int col[PER_WAVE];
-  __device__ __forceinline__ void init() {
-    const int wv = threadIdx.x >> 6, lane = lane_id();
+  int wv, stride;
+  uint32_t voff[PER_WAVE];
+  __device__ __forceinline__ void slot(int j, int& r, int& c) const {
+    const int sl = 64 * (wv + 4 * j) + lane_id();
+    r = sl / SPR;
+    const int cc = sl % SPR;
+    int chunk;
+    if constexpr (L::LINEAR) {
+      chunk = cc < L::CH ? cc : 0;
+    } else {
+      chunk = cc ^ L::swz(r);
+    }
+    c = 8 * chunk;
+  }
+  __device__ __forceinline__ void init(int row_stride) {
+    wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    stride = row_stride;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int slot = 64 * (wv + 4 * j) + lane;
-      const int r = slot / SPR, c = slot % SPR;
-      int chunk;
-      if constexpr (L::LINEAR) {
-        chunk = c < L::CH ? c : 0;
-      } else {
-        chunk = c ^ L::swz(r);
-      }
-      row[j] = r;
-      col[j] = 8 * chunk;
+      int r, c;
+      slot(j, r, c);
+      voff[j] = 2u * (uint32_t)(r * stride + c);
     }
   }
-  // gbase: element pointer of tile row 0, column 0 (wave-uniform); rows are
-  // row_stride elements apart
-  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int row_stride, int nvalid) const {
-    const int wv = threadIdx.x >> 6;
+  // gbase: element pointer of tile row 0, column 0 (wave-uniform)
+  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int nvalid) const {
+    const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)gbase);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile)) + 1024u * wv;
+    if (nvalid >= ROWS) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int r = min(row[j], nvalid - 1);
-      dma_to_lds<16>(gbase, 2u * (uint32_t)(r * row_stride + col[j]), lds_tile + 1024 * (wv + 4 * j));
+      for (int j = 0; j < PER_WAVE; ++j) dma_raw<16>(sb, voff[j], m0 + 4096u * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        int r, c;
+        slot(j, r, c);
+        dma_raw<16>(sb, 2u * (uint32_t)(min(r, nvalid - 1) * stride + c), m0 + 4096u * j);
+      }
     }
   }
 };
@@ -186,7 +213,8 @@ struct DmaTile {
 // The same direct staging for an XorTile<D> of ROWS rows by a workgroup of NW
 // waves.  Wave w's instruction j fills slots 64 (w + NW j) .. + 63, i.e. rows
 // r0 + RSTEP j of the lane; the XOR pattern repeats every PERIOD instructions,
-// so only the row of j = 0 and PERIOD column offsets are kept per lane.
+// so a full tile needs PERIOD lane offsets, the rest of instruction j's
+// offset (RSTEP j rows) being added to the wave-uniform base.
 template <int D, int ROWS, int NW>
 struct DmaXor {
   using L = XorTile<D>;
@@ -196,20 +224,31 @@ struct DmaXor {
   static constexpr int RSTEP = 64 * NW / SPR;
   static constexpr int PERIOD = RSTEP % 16 == 0 ? 1 : RSTEP % 8 == 0 ? 2 : RSTEP % 4 == 0 ? 4 : 16;
   static_assert(64 % SPR == 0 && NINST % NW == 0, "tile must split evenly over the waves");
-  int r0;
-  int col[PERIOD];
-  __device__ __forceinline__ void init() {
-    const int wv = threadIdx.x >> 6, lane = lane_id();
-    r0 = 64 * wv / SPR + lane / SPR;
+  int wv, stride;
+  uint32_t vb[PERIOD];
+  __device__ __forceinline__ int r0() const { return 64 * wv / SPR + lane_id() / SPR; }
+  __device__ __forceinline__ int col(int p) const { return 8 * ((lane_id() % SPR) ^ L::swz(r0() + RSTEP * p)); }
+  __device__ __forceinline__ void init(int row_stride) {
+    wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    stride = row_stride;
 #pragma unroll
-    for (int p = 0; p < PERIOD; ++p) col[p] = 8 * ((lane % SPR) ^ L::swz(r0 + RSTEP * p));
+    for (int p = 0; p < PERIOD; ++p) vb[p] = 2u * (uint32_t)(r0() * stride + col(p));
   }
-  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int row_stride, int nvalid) const {
-    const int wv = threadIdx.x >> 6;
+  // instructions J0 .. J1 - 1 of this wave's share (all by default)
+  template <int J0 = 0, int J1 = PER_WAVE>
+  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* gbase, int nvalid) const {
+    const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)gbase);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile)) + 1024u * wv;
+    if (nvalid >= ROWS) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int r = min(r0 + RSTEP * j, nvalid - 1);
-      dma_to_lds<16>(gbase, 2u * (uint32_t)(r * row_stride + col[j % PERIOD]), lds_tile + 1024 * (wv + NW * j));
+      for (int j = J0; j < J1; ++j)
+        dma_raw<16>(sb + 2ull * RSTEP * j * (uint64_t)stride, vb[j % PERIOD], m0 + 1024u * NW * j);
+    } else {
+#pragma unroll
+      for (int j = J0; j < J1; ++j) {
+        const int r = min(r0() + RSTEP * j, nvalid - 1);
+        dma_raw<16>(sb, 2u * (uint32_t)(r * stride + col(j % PERIOD)), m0 + 1024u * NW * j);
+      }
     }
   }
 };

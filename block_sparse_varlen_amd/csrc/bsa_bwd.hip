@@ -93,29 +93,32 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
 
   Dma dma;
-  dma.init();
+  dma.init(a.n2 * D);
   Operands<L, D> of;
   of.init();
-  // `ld` loads the sub-tile after the one `cp` computes (LDS double buffer)
-  SubTileWalk<> ld, cp;
+  // `ld` walks the sub-tiles and loads each one a step before it is computed
+  // (LDS double buffer); key_next is the first key of the last one issued
+  SubTileWalk<> ld;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
-  cp = ld;
+  int key_next = 0;
   auto issue = [&](int stage) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.key();
+    key_next = key0;
     const int64_t off = kv_tile_offset<false>(a.seq, nullptr, it.b, it.g, key0, a.n2, D, 0, 0, 0);
-    dma.issue(st, kp + off, a.n2 * D, it.skv - key0);
-    dma.issue(st + TILE, vp + off, a.n2 * D, it.skv - key0);
+    dma.issue(st, kp + off, it.skv - key0);
+    dma.issue(st + TILE, vp + off, it.skv - key0);
     ld.next();
   };
-  if (ld.valid()) issue(0);
+  bool more = ld.valid();
+  if (more) issue(0);
   int stage = 0;
-  while (cp.valid()) {
+  while (more) {
+    const int key0 = key_next;     // the sub-tile computed in this step
     wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
-    if (ld.valid()) issue(stage ^ 1);
-    const int key0 = cp.key();
-    cp.next();
+    more = ld.valid();
+    if (more) issue(stage ^ 1);
     settle_scalar_loads();
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
@@ -268,9 +271,9 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* dop = reinterpret_cast<const uint16_t*>(a.dout);
 
-  // Two cursors over the same (head, q-block, half) sequence: `ld` issues the
-  // loads of the next tile while `cp` computes the current one.
-  ColWalk ld, cp;
+  // `ld` walks the (head, q-block, half) sequence and loads each tile a step
+  // before it is computed; r0_next is the first row of the last one issued.
+  ColWalk ld;
   ld.col_ptr = a.col_ptr;
   ld.qrows = a.qrows;
   ld.group = a.group;
@@ -286,35 +289,37 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   ld.half = 0;
   ld.open(0);
   ld.settle();
-  cp = ld;
+  int r0_next = 0;
 
   Dma dma;
-  dma.init();
+  dma.init(qstride);
   Operands<QL, D> of;
   of.init();
   auto issue = [&](int stage) {
     char* st = smem + stage * STAGE;
     const int h = g * a.group + ld.hh;
     const int r0 = ld.row0();
+    r0_next = r0;
     const int nvalid = sq - r0;
     const int64_t off = (q0 + r0) * (int64_t)qstride + (int64_t)h * D;
-    dma.issue(st, qp + off, qstride, nvalid);
-    dma.issue(st + TILE, dop + off, qstride, nvalid);
+    dma.issue(st, qp + off, nvalid);
+    dma.issue(st + TILE, dop + off, nvalid);
     float* stat = reinterpret_cast<float*>(st + 2 * TILE);
     // lse (wave 0) and D (wave 1) of the tile's rows
     dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.dl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     ld.next();
   };
 
-  if (ld.valid()) issue(0);
+  bool more = ld.valid();
+  if (more) issue(0);
   int stage = 0;
-  while (cp.valid()) {
+  while (more) {
+    const int r0 = r0_next;     // the tile computed in this step
+    const int nrows = sq - r0;  // its valid rows (may exceed QS)
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // both waves' loads landed; the other stage is no longer read
-    if (ld.valid()) issue(stage ^ 1);
-    const int r0 = cp.row0();
-    const int nrows = sq - r0;  // valid rows of this tile (may exceed QS)
-    cp.next();
+    more = ld.valid();
+    if (more) issue(stage ^ 1);
     settle_scalar_loads();
     char* ql = smem + stage * STAGE;
     char* dl_ = ql + TILE;

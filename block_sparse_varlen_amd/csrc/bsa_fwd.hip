@@ -81,34 +81,36 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 
   DmaTile<KL, D, KT> kdma;
   DmaTile<VL, D, KT> vdma;
-  kdma.init();
-  vdma.init();
+  kdma.init(a.n2 * D);
+  vdma.init(a.n2 * D);
   Operands<KL, D> ofk;
   Operands<VL, D> ofv;
   ofk.init();
   ofv.init();
-  // `ld` loads the sub-tile after the one `cp` computes (LDS double buffer)
-  SubTileWalk<> ld, cp;
+  // `ld` walks the sub-tiles and loads each one a step before it is computed
+  // (LDS double buffer); key_next is the first key of the last one issued
+  SubTileWalk<> ld;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
-  cp = ld;
-  const int kvrow = a.n2 * D;
+  int key_next = 0;
   auto issue = [&](int stage) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.key();
+    key_next = key0;
     const int64_t off = kv_tile_offset<PAGED>(a.seq, a.block_table, it.b, it.g, key0, a.n2, D, a.page_size,
                                               a.max_pages, a.page_stride);
-    kdma.issue(st, kbase_p + off, kvrow, it.skv - key0);
-    vdma.issue(st + KTILE, vbase_p + off, kvrow, it.skv - key0);
+    kdma.issue(st, kbase_p + off, it.skv - key0);
+    vdma.issue(st + KTILE, vbase_p + off, it.skv - key0);
     ld.next();
   };
-  if (ld.valid()) issue(0);
+  bool more = ld.valid();
+  if (more) issue(0);
   int stage = 0;
-  while (cp.valid()) {
+  while (more) {
+    const int key0 = key_next;     // the sub-tile computed in this step
     wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
-    if (ld.valid()) issue(stage ^ 1);
-    const int key0 = cp.key();
-    cp.next();
+    more = ld.valid();
+    if (more) issue(stage ^ 1);
     settle_scalar_loads();
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + KTILE;
