@@ -182,8 +182,9 @@ struct DmaTile {
     }
     c = 8 * chunk;
   }
+  // the copying waves are waves 0..3 of the workgroup, or of a 4-wave group of it
   __device__ __forceinline__ void init(int row_stride) {
-    wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wv = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
     stride = row_stride;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
@@ -228,8 +229,9 @@ struct DmaXor {
   uint32_t vb[PERIOD];
   __device__ __forceinline__ int r0() const { return 64 * wv / SPR + lane_id() / SPR; }
   __device__ __forceinline__ int col(int p) const { return 8 * ((lane_id() % SPR) ^ L::swz(r0() + RSTEP * p)); }
+  // the copying waves are waves 0 .. NW-1 of the workgroup, or of an NW-wave group of it
   __device__ __forceinline__ void init(int row_stride) {
-    wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wv = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW);
     stride = row_stride;
 #pragma unroll
     for (int p = 0; p < PERIOD; ++p) vb[p] = 2u * (uint32_t)(r0() * stride + col(p));
@@ -309,6 +311,89 @@ struct SubTileWalk {
       ++e;
       s = 0;
     }
+  }
+};
+
+// The same walk with the row's block list held in a VGPR (lane l holds entry
+// base + l), so handing out a sub-tile is a lane read instead of a scalar
+// memory round trip on the critical path of the tile copies.  Rows of more
+// than 64 entries reload the register per 64 entries and wait for that load
+// on the spot (rare), which leaves the compiler no pending load of it to wait
+// for elsewhere -- such a wait would also drain the tile copies in flight.
+template <int T = KT>
+struct RegTileWalk {
+  const int32_t* cols;
+  int e, e1, base, s, nsub, by, kend;
+  int colv;
+  // The caller waits for the initial load (any vmcnt wait covering it) before
+  // the first take<false>(); take<true>() reads its entry with a scalar load
+  // instead, for a first sub-tile issued before that wait.
+  __device__ __forceinline__ void init(const int32_t* c, int e0, int e_end, int by_, int kend_) {
+    cols = c;
+    e = e0;
+    e1 = e_end;
+    base = e0;
+    s = 0;
+    by = by_;
+    nsub = by_ / T;
+    kend = kend_;
+    colv = e0 + lane_id() < e_end ? c[e0 + lane_id()] : 0;
+  }
+  __device__ __forceinline__ bool valid() const { return e < e1; }
+  // first key of the current sub-tile; advances to the next one
+  template <bool SCALAR = false>
+  __device__ __forceinline__ int take() {
+    int c;
+    if constexpr (SCALAR) {
+      c = ldu(cols, e);
+    } else {
+      if (__builtin_expect(e - base >= 64, 0)) {
+        base += 64;
+        colv = base + lane_id() < e1 ? cols[base + lane_id()] : 0;
+        wait_vmcnt<0>();
+        pin(colv);
+      }
+      c = __builtin_amdgcn_readlane(colv, e - base);
+    }
+    const int key = c * by + s * T;
+    ++s;
+    if (s >= nsub || key + T >= kend) {
+      ++e;
+      s = 0;
+    }
+    return key;
+  }
+};
+
+// Element offsets of key tiles of KV head g of sequence b: packed rows
+// (cu_kv[b] + key) * N2 + g, computed from a per-item base with no memory
+// access, or through the page table (block_table[b, key / page_size], key %
+// page_size) for paged caches.
+template <bool PAGED>
+struct KvAddr {
+  int64_t row0, step;
+  const int32_t* block_table;
+  int b, g, n2, d, page_size, max_pages;
+  int64_t page_stride;
+  __device__ __forceinline__ void init(const SeqArgs& sq, const int32_t* bt, int b_, int g_, int n2_, int d_,
+                                       int page_size_, int max_pages_, int64_t page_stride_) {
+    block_table = bt;
+    b = b_;
+    g = g_;
+    n2 = n2_;
+    d = d_;
+    page_size = page_size_;
+    max_pages = max_pages_;
+    page_stride = page_stride_;
+    step = (int64_t)n2_ * d_;
+    row0 = PAGED ? 0 : (ldu(sq.cu_kv, b_) * n2_ + g_) * (int64_t)d_;
+  }
+  __device__ __forceinline__ int64_t off(int key0) const {
+    if constexpr (PAGED)
+      return ((int64_t)ldu(block_table, (int64_t)b * max_pages + key0 / page_size)) * page_stride +
+             ((int64_t)(key0 % page_size) * n2 + g) * d;
+    else
+      return row0 + key0 * step;
   }
 };
 

@@ -98,28 +98,29 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   of.init();
   // `ld` walks the sub-tiles and loads each one a step before it is computed
   // (LDS double buffer); key_next is the first key of the last one issued
-  SubTileWalk<> ld;
+  RegTileWalk<> ld;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
+  KvAddr<false> kva;
+  kva.init(a.seq, nullptr, it.b, it.g, a.n2, D, 0, 0, 0);
   int key_next = 0;
-  auto issue = [&](int stage) {
+  // the first sub-tile goes out before the block list register has landed
+  auto issue = [&](int stage, auto first) {
     char* st = smem + stage * STAGE;
-    const int key0 = ld.key();
+    const int key0 = ld.template take<decltype(first)::value>();
     key_next = key0;
-    const int64_t off = kv_tile_offset<false>(a.seq, nullptr, it.b, it.g, key0, a.n2, D, 0, 0, 0);
+    const int64_t off = kva.off(key0);
     dma.issue(st, kp + off, it.skv - key0);
     dma.issue(st + TILE, vp + off, it.skv - key0);
-    ld.next();
   };
   bool more = ld.valid();
-  if (more) issue(0);
+  if (more) issue(0, std::true_type{});
   int stage = 0;
   while (more) {
     const int key0 = key_next;     // the sub-tile computed in this step
     wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
     more = ld.valid();
-    if (more) issue(stage ^ 1);
-    settle_scalar_loads();
+    if (more) issue(stage ^ 1, std::false_type{});
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
 #pragma unroll
