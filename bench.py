@@ -30,6 +30,14 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 409
 METRIC = "fwd & bwd TFLOP/s over selected blocks; % of MI355X bf16 MFMA peak"
 WORKLOAD = "long-context block-sparse fwd+bwd: TND 2x16384, N1=N2=16, D=128, bf16, 128x128 blocks, " \
            "block-causal mask (diagonal + 4 preceding + 8 random earlier blocks per q-block)"
+# other workloads for --workload (not the default line): the rest of the
+# benchmark configurations, run fwd + bwd
+OTHER_WORKLOADS = {
+    2: "dense varlen causal fwd+bwd: TND, B=4, lengths U{512..4096}, N=16, D=128, bf16, all blocks",
+    3: "sabi block-sparse prefill fwd+bwd: B=1, N=32, S=32768, D=128, bf16, block (128,512), keep U{1..16}",
+    4: "GQA + paged-KV block-sparse fwd+bwd: B=8, lengths U{1024..8192}, N1=32, N2=8, D=128, bf16, "
+       "128-token pages, idx top-16 (counts U{4..16}), causal",
+}
 # GEMMs each kernel performs out of the counted ones: fwd = QK^T, PV (4 r c D);
 # dK/dV kernel = S, dP, dV, dK (8 r c D); dQ kernel = dQ (2 r c D; its
 # recomputation of S and dP is not counted).
@@ -53,7 +61,7 @@ def kernel_source_sha(kernel: str) -> str:
 def visited_rcd(case, idx):
     """Sum over visited (q-head, q-block, kv-block) pairs of r * c * D."""
     lens_q = np.diff(case.cu_q)
-    lens_kv = np.diff(case.cu_kv)
+    lens_kv = case.seqused_kv if case.paged else np.diff(case.cu_kv)
     nqb = -(-lens_q // case.bx)
     qbase = np.concatenate([[0], np.cumsum(nqb)])
     TQB, R = idx["TQB"], idx["R"]
@@ -164,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5],
+                    help="benchmark configuration (default 5, the long-context workload the metric is quoted on)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 512 MiB elementwise copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -178,7 +188,8 @@ def main():
 
     torch.cuda.set_device(0)
     print("bench: generating inputs", file=sys.stderr, flush=True)
-    case = synth.config5()
+    case = synth.CONFIGS[args.workload](with_dout=True) if args.workload in (3, 4) else synth.CONFIGS[args.workload]()
+    workload = WORKLOAD if args.workload == 5 else OTHER_WORKLOADS[args.workload]
     dc = DeviceCase(case, with_bwd=True)
     idx = dc.index(False)
     rcd = visited_rcd(case, idx)
@@ -245,7 +256,7 @@ def main():
     alg = ALG_FLOPS_PER_RCD[dominant] * rcd
     achieved = alg / (per_kernel[dominant]["avg_ms"] * 1e-3) / 1e12
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if args.workload == 5 and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
         ent = tr.get(dominant)
@@ -265,8 +276,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V/dO, seeded block mask)",
-        "config": {"workload": WORKLOAD, "global_batch": case.B, "seq_len": int(np.diff(case.cu_q).max()),
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, seeded block selection)",
+        "config": {"workload": workload, "global_batch": case.B, "seq_len": int(np.diff(case.cu_q).max()),
                    "heads": case.N1, "head_dim": case.D, "block_shape": [case.bx, case.by],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),

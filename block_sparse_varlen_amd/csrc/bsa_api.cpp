@@ -55,7 +55,6 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
 }
 
 bsa_status_t check_bwd_variant(const bsa_problem_t* p) {
-  if (p->kv_layout == BSA_KV_PAGED) return BSA_ERR_INNER;
   if (p->block_y % 128 != 0) return BSA_ERR_INNER;
   return BSA_OK;
 }
@@ -406,7 +405,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   if (p->total_kv > 0 && (!k || !v || !dk || !dv)) return BSA_ERR_PARAM_NULLPTR;
   st = check_index_ptrs(p, cu_q, cu_kv, seqused, sparse, count);
   if (st != BSA_OK) return st;
-  (void)block_table;
+  if (p->kv_layout == BSA_KV_PAGED && !block_table) return BSA_ERR_PARAM_NULLPTR;
   if (!workspace) return BSA_ERR_PARAM_NULLPTR;
   if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
 
@@ -450,6 +449,10 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.col_ptr = ip.col_ptr;
   a.qrows = ip.qrows;
   a.work_kv = ip.work_kv;
+  a.block_table = block_table;
+  a.page_size = p->kv_layout == BSA_KV_PAGED ? p->page_size : 0;
+  a.max_pages = p->kv_layout == BSA_KV_PAGED ? p->max_pages_per_seq : 0;
+  a.page_stride = p->kv_layout == BSA_KV_PAGED ? p->page_stride : 0;
   a.n1 = p->num_heads_q;
   a.n2 = p->num_heads_kv;
   a.group = group;

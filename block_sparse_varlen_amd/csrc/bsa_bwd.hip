@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 //   P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T o (dP^T - D)
 //   dQ^T += K^T dS^T                       (K^T via LDS transpose loads)
 
-template <typename MF, int D, bool CAUSAL>
+template <typename MF, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   using L = XorTile<D>;  // K: read row-major (S^T) and transposed (dQ^T); V: row-major (dP^T)
   constexpr int TILE = L::template bytes<KT>();
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   // (LDS double buffer); key_next is the first key of the last one issued
   RegTileWalk<> ld;
   ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
-  KvAddr<false> kva;
-  kva.init(a.seq, nullptr, it.b, it.g, a.n2, D, 0, 0, 0);
+  KvAddr<PAGED> kva;
+  kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   int key_next = 0;
   // the first sub-tile goes out before the block list register has landed
   auto issue = [&](int stage, auto first) {
@@ -217,7 +217,7 @@ struct ColWalk {
 constexpr int DKDV_WAVES = 2;   // a workgroup's waves, 64 keys each
 constexpr int DKDV_STAGES = 2;  // LDS ring depth (two workgroups per CU share the LDS)
 
-template <typename MF, int D, bool CAUSAL>
+template <typename MF, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   using QL = XorTile<D>;  // Q and dO: read row-major (S, dP) and transposed (dK^T, dV^T)
   constexpr int TILE = QL::template bytes<QS>();
@@ -239,8 +239,16 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   const int kb = kg - ldu(a.kbase, b);
   const int64_t q0 = ldu(a.seq.cu_q, b);
   const int sq = (int)(ldu(a.seq.cu_q, b + 1) - q0);
-  const int64_t kv0 = ldu(a.seq.cu_kv, b);
-  const int skv = (int)(ldu(a.seq.cu_kv, b + 1) - kv0);
+  // Rows of this tile's keys: packed rows kv0 + key, or (page, slot) through
+  // the block table (looked up per lane: a tile may span pages).
+  int64_t kv0 = 0;
+  int skv;
+  if constexpr (PAGED) {
+    skv = ldu(a.seq.seqused_kv, b);
+  } else {
+    kv0 = ldu(a.seq.cu_kv, b);
+    skv = (int)(ldu(a.seq.cu_kv, b + 1) - kv0);
+  }
   const int key_lo = kb * a.seq.by + sub * 128;
   if (key_lo >= skv) return;
   const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,11 +256,20 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   const int key_w = key_lo + 64 * wv + (lane & 31);
   const int qoff = skv - sq;
   const int64_t kvstride = (int64_t)a.n2 * D;
+  // element offset of key `key` (< skv) of this tile, head g, column 0
+  auto key_row = [&](int key) -> int64_t {
+    if constexpr (PAGED) {
+      const int64_t page = a.block_table[(int64_t)b * a.max_pages + key / a.page_size];
+      return page * a.page_stride + (int64_t)(key % a.page_size) * kvstride + (int64_t)g * D;
+    } else {
+      return (kv0 + key) * kvstride + (int64_t)g * D;
+    }
+  };
   u32x4_t kf[2][NKK], vf[2][NKK];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int key = key_w + 32 * n;
-    const int64_t krow = (kv0 + key) * kvstride + (int64_t)g * D + 8 * (lane >> 5);
+    const int64_t krow = (PAGED && key >= skv ? 0 : key_row(key)) + 8 * (lane >> 5);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       kf[n][kk] = key < skv ? gload16(reinterpret_cast<const uint16_t*>(a.k) + krow + 16 * kk) : zero_u4();
@@ -413,7 +430,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   for (int n = 0; n < 2; ++n) {
     const int key = key_w + 32 * n;
     if (key < skv) {
-      const int64_t orow = (kv0 + key) * kvstride + (int64_t)g * D;
+      const int64_t orow = key_row(key);
       uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + orow;
       uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + orow;
 #pragma unroll
@@ -425,23 +442,30 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   }
 }
 
+template <typename MF, int D, bool PAGED>
+hipError_t launch_dq_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
+  if (a.seq.causal)
+    k_bwd_dq<MF, D, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
+  else
+    k_bwd_dq<MF, D, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
 template <typename MF, int D>
 hipError_t launch_dq_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
+  return a.seq.seqused_kv ? launch_dq_p<MF, D, true>(a, grid, st) : launch_dq_p<MF, D, false>(a, grid, st);
+}
+template <typename MF, int D, bool PAGED>
+hipError_t launch_dkdv_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
   if (a.seq.causal)
-    k_bwd_dq<MF, D, true><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_bwd_dkdv<MF, D, true, PAGED><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
   else
-    k_bwd_dq<MF, D, false><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_bwd_dkdv<MF, D, false, PAGED><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
   return hipGetLastError();
 }
 template <typename MF, int D>
 hipError_t launch_dkdv_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.seq.causal)
-    k_bwd_dkdv<MF, D, true><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
-  else
-    k_bwd_dkdv<MF, D, false><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
-  return hipGetLastError();
+  return a.seq.seqused_kv ? launch_dkdv_p<MF, D, true>(a, grid, st) : launch_dkdv_p<MF, D, false>(a, grid, st);
 }
-
 }  // namespace
 
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, hipStream_t st) {

@@ -144,6 +144,9 @@ struct BwdArgs {
   const int32_t* col_ptr;
   const int32_t* qrows;
   const int32_t* work_kv;
+  const int32_t* block_table;  // paged K/V (and dK/dV): [B, max_pages]
+  int32_t page_size, max_pages;
+  int64_t page_stride;     // elements
   int32_t n1, n2, group, heads_per_row, hs;
   int32_t sub_tiles;       // block_y / 128 (dK/dV tiles per KV block)
   float sigma;

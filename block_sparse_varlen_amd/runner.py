@@ -82,7 +82,7 @@ class DeviceCase:
         T, N1, D = int(case.cu_q[-1]), case.N1, case.D
         self.out = torch.empty((T, N1, D), dtype=tdt, device=device)
         self.lse = torch.empty((T, N1), dtype=torch.float32, device=device)
-        want_bwd = (self.dout is not None and not case.paged) if with_bwd is None else with_bwd
+        want_bwd = (self.dout is not None) if with_bwd is None else with_bwd
         fwd_b, bwd_b = bsa_get_workspace_size(self.p, True, want_bwd)
         self.ws_fwd_bytes = fwd_b
         self.ws_bwd_bytes = bwd_b

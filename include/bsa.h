@@ -153,9 +153,12 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
 
 /* Stage 2, backward.  Inputs as bsa_fwd plus `out` and `lse` from the forward
  * pass and `dout` [T_q, N1, D].  Outputs dq [T_q, N1, D], dk and dv with k's
- * shape (TND only: the paged layout returns BSA_ERR_INNER from stage 1's
- * bwd_bytes query and from this call).  dQ is computed by a separate
- * Q-block-major pass, so results are deterministic run to run. */
+ * shape.  In the paged layout dk / dv are written at the (page, slot) of every
+ * key below seqused_kv[b] of every sequence (zeros for keys no row attends)
+ * and the rest of the page pool is left as it was; two sequences must not
+ * share a page (their gradients would be written, not summed).  Needs
+ * block_y a multiple of 128 (else BSA_ERR_INNER).  dQ is computed by a
+ * separate Q-block-major pass, so results are deterministic run to run. */
 bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse,
                      const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,

@@ -92,11 +92,16 @@ def test_stage1_nullptr():
     assert status(good(), fwd=False, bwd=False) == bsa.BSA_ERR_PARAM_NULLPTR
 
 
-def test_paged_backward_not_compiled():
+def test_paged_backward_sizes():
     p = good(kv_layout=bsa.BSA_KV_PAGED, page_size=128, max_pages_per_seq=4, page_stride=128 * 2 * 128,
              total_kv=10)
     assert status(p, fwd=True, bwd=False) == bsa.BSA_OK
-    assert status(p, fwd=False, bwd=True) == bsa.BSA_ERR_INNER
+    assert status(p, fwd=False, bwd=True) == bsa.BSA_OK
+    p64 = good(kv_layout=bsa.BSA_KV_PAGED, page_size=64, max_pages_per_seq=8, page_stride=64 * 2 * 128,
+               total_kv=10)
+    assert status(p64, fwd=False, bwd=True) == bsa.BSA_OK
+    # the backward's KV tiles are 128 keys: block_y = 64 has no backward variant
+    assert status(good(block_y=64), fwd=False, bwd=True) == bsa.BSA_ERR_INNER
 
 
 def _fwd_status(p, ws_bytes=1 << 30, **ptrs):

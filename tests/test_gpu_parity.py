@@ -64,6 +64,15 @@ def bwd_cases():
                              sparse_heads=4, width=5),
         "none_causal_f16": R(205, lens_q=[129, 384, 1], N1=2, D=128, dtype="f16", kind="none", causal=True),
         "none_sq_lt_skv": R(206, lens_q=[100], lens_kv=[1000], N1=2, D=128, kind="none", causal=True),
+        # paged K/V (dK/dV written in the page layout): GQA with a shared
+        # pattern, pages of 64 keys (a 128-key tile spans two pages), pages of
+        # 256 keys, and per-q-head sabi rows
+        "idx_paged_causal_gqa": R(207, lens_q=[500, 310], lens_kv=[400, 700], N1=4, N2=2, D=128, kind="idx",
+                                  sparse_heads=2, causal=True, paged=True),
+        "mask_paged_ps64_f16": R(208, lens_q=[300, 200], lens_kv=[333, 450], N1=2, D=64, dtype="f16",
+                                 kind="mask", paged=True, page_size=64),
+        "sabi_perhead_gqa_paged_ps256": R(209, lens_q=[260, 333], N1=4, N2=2, D=128, kind="sabi",
+                                          sparse_heads=4, paged=True, page_size=256, causal=True),
     }
 
 
@@ -103,20 +112,32 @@ def rel_fro(x, r):
     return d / n if n > 0 else d
 
 
+def kv_valid(case):
+    """Positions of k/v holding a sequence's key: every TND row, or the
+    (page, slot) pairs of keys below seqused_kv (the generator leaves NaN in
+    the rest of the page pool)."""
+    if not case.paged:
+        return np.ones(case.k.shape[:1], dtype=bool)
+    return ~np.isnan(case.k[:, :, 0, 0])
+
+
 def check_bwd(case, dc, tag=""):
     dq = dc.dq.float().cpu().numpy()
     dk = dc.dk.float().cpu().numpy()
     dv = dc.dv.float().cpu().numpy()
     rq, rk, rv = oracle.backward(case)
-    eq, ek, ev = rel_fro(dq, rq), rel_fro(dk, rk), rel_fro(dv, rv)
+    val = kv_valid(case)
+    eq, ek, ev = rel_fro(dq, rq), rel_fro(dk[val], rk[val]), rel_fro(dv[val], rv[val])
     say(f"  {tag}: rel_fro dq={eq:.3e} dk={ek:.3e} dv={ev:.3e}")
     tol = TOL_G[case.dtype]
     assert eq <= tol and ek <= tol and ev <= tol
+    # positions of the page pool that hold no key are left as they were (NaN here)
+    assert np.all(np.isnan(dk[~val])) and np.all(np.isnan(dv[~val]))
     # structural zeros: q rows with no allowed key (lse = +inf) get dq = 0;
     # keys no row reaches (dv row exactly 0 in the oracle) get dk = dv = 0
     _, lse_r = oracle.forward(case)
     assert np.all(dq[np.isinf(lse_r)] == 0)
-    unreached = np.all(rv == 0, axis=-1)
+    unreached = np.all(rv == 0, axis=-1) & val[..., None]
     assert np.all(dk[unreached] == 0) and np.all(dv[unreached] == 0)
 
 
@@ -131,7 +152,7 @@ def nan_fill(*ts):
 def test_index_bit_exact(name):
     case = FWD[name]
     say(f"index {name}")
-    with_csc = not case.paged and case.by % 128 == 0  # backward variants need 128-key tiles
+    with_csc = case.by % 128 == 0  # backward variants need 128-key tiles
     dc = DeviceCase(case, with_bwd=with_csc)
     got = dc.index(with_csc)
     ref = oracle.index_products(case, with_csc=with_csc)
@@ -247,18 +268,26 @@ def test_fwd_config(n):
     check_fwd(case, dc, sample=sample, tag=f"config{n}")
 
 
+@functools.lru_cache(maxsize=1)
+def _cfg_bwd(n):
+    return synth.CONFIGS[n](with_dout=True) if n in (3, 4) else synth.CONFIGS[n]()
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("n", [1, 2, 5])
+@pytest.mark.parametrize("n", [1, 2, 4, 5])
 def test_bwd_config(n):
-    case = _cfg(n)
+    case = _cfg_bwd(n)
     say(f"config {n}: bwd on GPU")
     dc = DeviceCase(case, with_bwd=True)
     dc.fwd()
     nan_fill(dc.dq, dc.dk, dc.dv)
     dc.bwd()
     torch.cuda.synchronize()
-    for t in (dc.dq, dc.dk, dc.dv):
-        assert not torch.isnan(t).any()
+    assert not torch.isnan(dc.dq).any()
+    val = torch.from_numpy(kv_valid(case)).to(dc.dk.device)
+    for t in (dc.dk, dc.dv):  # every key position written; the rest of a page pool untouched
+        assert not torch.isnan(t[val]).any()
+        assert torch.isnan(t[~val]).all()
     got = dc.index(True)
     idx = oracle.index_products(case, with_csc=True)
     for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
@@ -268,7 +297,8 @@ def test_bwd_config(n):
         return
     rng = np.random.default_rng(100 + n)
     rows = _sample_rows(case, idx, 12, 50 + n)
-    kbase = np.concatenate([[0], np.cumsum([-(-int(s) // case.by) for s in np.diff(case.cu_kv)])])
+    skv = case.seqused_kv if case.paged else np.diff(case.cu_kv)
+    kbase = np.concatenate([[0], np.cumsum([-(-int(s) // case.by) for s in skv])])
     kvs = set()
     for it in list(idx["work_kv"][:3]) + list(rng.choice(len(idx["work_kv"]), 6, replace=False)):
         g, kg = divmod(int(it), idx["TKB"])
@@ -281,14 +311,15 @@ def test_bwd_config(n):
     selq = ~np.isnan(rq[..., 0])
     tol = TOL_G[case.dtype]
     eq = rel_fro(dq[selq], rq[selq])
-    keys = []
+    keys = []  # (row index tuple, kv head) of every key of the sampled KV blocks
     for (b, g, kb) in kvs:
-        k0 = int(case.cu_kv[b]) + kb * case.by
-        k1 = min(int(case.cu_kv[b + 1]), k0 + case.by)
-        keys += [(j, g) for j in range(k0, k1)]
-    kj = np.array([x[0] for x in keys])
-    kgs = np.array([x[1] for x in keys])
-    ek = rel_fro(dk[kj, kgs], rk[kj, kgs])
-    ev = rel_fro(dv[kj, kgs], rv[kj, kgs])
+        for j in range(kb * case.by, min(int(skv[b]), (kb + 1) * case.by)):
+            if case.paged:
+                keys.append(((int(case.block_table[b, j // case.page_size]), j % case.page_size), g))
+            else:
+                keys.append(((int(case.cu_kv[b]) + j,), g))
+    ix = tuple(np.array([k[0][i] for k in keys]) for i in range(len(keys[0][0]))) + (np.array([k[1] for k in keys]),)
+    ek = rel_fro(dk[ix], rk[ix])
+    ev = rel_fro(dv[ix], rv[ix])
     say(f"  config{n}: rel_fro dq={eq:.3e} dk={ek:.3e} dv={ev:.3e} (sampled)")
     assert eq <= tol and ek <= tol and ev <= tol
