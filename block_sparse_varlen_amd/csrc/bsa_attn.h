@@ -9,7 +9,7 @@
 namespace bsa {
 
 constexpr int KT = 64;   // keys per sub-tile of the Q-major kernels
-constexpr int QT = 128;  // query rows per Q-major work item (4 waves x 32)
+constexpr int QT = 128;  // query rows per Q-major work item (4 waves x 32); block_x is a multiple
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  xcd_item maps dispatch index `bid` to a work item so that every XCD
@@ -23,7 +23,7 @@ __device__ __forceinline__ int64_t xcd_item(int64_t bid) {
   return (k / XCD_SEG) * (NUM_XCD * XCD_SEG) + x * XCD_SEG + (k % XCD_SEG);
 }
 
-// A Q-major work item: one q-block of one q-head.
+// A Q-major work item: a 128-row slice of one q-block of one q-head.
 struct QItem {
   int r;        // CSR row
   int h, g;     // q-head, kv-head
@@ -34,14 +34,19 @@ struct QItem {
   int nrows;    // valid query rows in the item
 };
 
-// item = slot * heads_per_row + j; slot indexes the longest-first row order.
+// item = (slot * heads_per_row + j) * (block_x / 128) + slice; slot indexes
+// the longest-first row order.  Returns false past the last item and for a
+// slice that starts past the sequence end (nothing to do).
 __device__ __forceinline__ bool decode_qitem(int64_t item, const int32_t* hdr, const int32_t* work,
                                              const int32_t* qb_seq, const int32_t* qbase, const SeqArgs& seq,
                                              int heads_per_row, int group, QItem& it) {
   const int R = ldu(hdr, H_R);
-  if (item >= (int64_t)R * heads_per_row) return false;
-  const int slot = (int)(item / heads_per_row);
-  const int jh = (int)(item - (int64_t)slot * heads_per_row);
+  const int slices = seq.bx / QT;
+  if (item >= (int64_t)R * heads_per_row * slices) return false;
+  const int64_t ritem = item / slices;
+  const int slice = (int)(item - ritem * slices);
+  const int slot = (int)(ritem / heads_per_row);
+  const int jh = (int)(ritem - (int64_t)slot * heads_per_row);
   it.r = ldu(work, slot);
   const int TQB = ldu(hdr, H_TQB);
   const int hs = it.r / TQB;
@@ -53,9 +58,9 @@ __device__ __forceinline__ bool decode_qitem(int64_t item, const int32_t* hdr, c
   it.q0 = ldu(seq.cu_q, it.b);
   it.sq = (int)(ldu(seq.cu_q, it.b + 1) - it.q0);
   it.skv = seq.seqused_kv ? ldu(seq.seqused_kv, it.b) : (int)(ldu(seq.cu_kv, it.b + 1) - ldu(seq.cu_kv, it.b));
-  it.row_lo = it.qb * QT;
+  it.row_lo = it.qb * seq.bx + slice * QT;
   it.nrows = min(QT, it.sq - it.row_lo);
-  return true;
+  return it.nrows > 0;
 }
 
 // Staging of a [ROWS x D] 16-bit tile whose rows are `row_stride` elements
@@ -332,6 +337,10 @@ struct RegTileWalk {
     cols = c;
     e = e0;
     e1 = e_end;
+    // the list is ascending: drop trailing blocks that start at or past kend
+    // (only a slice of a q-block taller than 128 rows can end before the
+    // q-block's causal limit, so this loop rarely runs)
+    while (e1 > e0 && ldu(c, e1 - 1) * by_ >= kend_) --e1;
     base = e0;
     s = 0;
     by = by_;

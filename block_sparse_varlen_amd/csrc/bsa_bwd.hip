@@ -172,16 +172,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 constexpr int QS = 64;  // query rows per staged sub-tile
 
 // Walk over (q-head of the group, q-block of the tile's column list, 64-row
-// half of the q-block), skipping halves past the sequence end or entirely
-// above the causal limit of the tile's first key.
+// part of the q-block: block_x / 64 of them), skipping parts past the
+// sequence end or entirely above the causal limit of the tile's first key.
 struct ColWalk {
   const int32_t* col_ptr;
   const int32_t* qrows;
   int hh, e, e1, half;
-  int group, per_head, g, tkb, kg, sq, qoff, key_min, causal;
+  int group, per_head, g, tkb, kg, sq, qoff, key_min, causal, bx, halves;  // halves = bx / QS
   __device__ __forceinline__ int col(int h) const { return (per_head ? g * group + h : g) * tkb + kg; }
   __device__ __forceinline__ bool ok(int qb, int hf) const {
-    const int r0 = qb * 128 + hf * QS;
+    const int r0 = qb * bx + hf * QS;
     if (r0 >= sq) return false;
     if (causal && min(r0 + QS, sq) - 1 + qoff < key_min) return false;
     return true;
@@ -195,7 +195,7 @@ struct ColWalk {
     while (hh < group) {
       while (e < e1) {
         const int qb = ldu(qrows, e);
-        while (half < 2) {
+        while (half < halves) {
           if (ok(qb, half)) return;
           ++half;
         }
@@ -211,7 +211,7 @@ struct ColWalk {
     ++half;
     settle();
   }
-  __device__ __forceinline__ int row0() const { return ldu(qrows, e) * 128 + half * QS; }
+  __device__ __forceinline__ int row0() const { return ldu(qrows, e) * bx + half * QS; }
 };
 
 constexpr int DKDV_WAVES = 2;   // a workgroup's waves, 64 keys each
@@ -303,6 +303,8 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   ld.qoff = qoff;
   ld.key_min = key_lo;
   ld.causal = CAUSAL;
+  ld.bx = a.seq.bx;
+  ld.halves = a.seq.bx / QS;
   ld.hh = 0;
   ld.half = 0;
   ld.open(0);

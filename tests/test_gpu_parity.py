@@ -49,6 +49,10 @@ def fwd_cases():
                                     paged=True),
         "mask_d64_bf16_causal_qlong": R(109, lens_q=[700], lens_kv=[260], N1=2, D=64, kind="mask",
                                         causal=True, density=0.7),
+        # q-blocks taller than one 128-row work item
+        "mask_bx256_causal": R(111, lens_q=[700, 300], N1=2, D=128, kind="mask", bx=256, causal=True),
+        "idx_bx512_gqa_paged_by256": R(112, lens_q=[1100, 520], lens_kv=[900, 1300], N1=4, N2=2, D=128,
+                                       kind="idx", sparse_heads=2, bx=512, by=256, paged=True, page_size=256),
     }
 
 
@@ -73,6 +77,11 @@ def bwd_cases():
                                  kind="mask", paged=True, page_size=64),
         "sabi_perhead_gqa_paged_ps256": R(209, lens_q=[260, 333], N1=4, N2=2, D=128, kind="sabi",
                                           sparse_heads=4, paged=True, page_size=256, causal=True),
+        # q-blocks of 256 and 512 rows (several 128-row items, 64-row dK/dV parts)
+        "mask_bx256_causal_f16": R(210, lens_q=[700, 300], N1=2, D=64, dtype="f16", kind="mask", bx=256,
+                                   causal=True),
+        "sabi_bx512_by256_causal": R(211, lens_q=[1100, 520], lens_kv=[1300, 900], N1=2, D=128,
+                                     kind="sabi", bx=512, by=256, causal=True),
     }
 
 
