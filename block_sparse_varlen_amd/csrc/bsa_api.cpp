@@ -46,7 +46,7 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
   if (!(p->scale >= 0.0) || !std::isfinite(p->scale)) return BSA_ERR_PARAM_INVALID;
   if (p->flags != 0 || p->reserved != 0) return BSA_ERR_PARAM_INVALID;
   // valid descriptors without a compiled variant
-  if (p->block_x % 128 != 0 || p->block_x > 4096) return BSA_ERR_INNER;
+  if (p->block_x % 64 != 0 || p->block_x > 4096) return BSA_ERR_INNER;
   if (p->block_y % 64 != 0 || p->block_y > 4096) return BSA_ERR_INNER;
   if (p->kv_layout == BSA_KV_PAGED && p->page_size % 64 != 0) return BSA_ERR_INNER;
   if ((int64_t)p->max_seqlen_kv > (int64_t)p->block_y * 65536 || (int64_t)p->max_seqlen_q > (int64_t)p->block_x * 65536)
@@ -384,7 +384,7 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
   prof_begin(BSA_KERNEL_FWD, s);
-  e = launch_fwd(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * (p->block_x / 128)), s);
+  e = launch_fwd(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128)), s);
   prof_end(BSA_KERNEL_FWD, s);
   return from_hip(e);
 }
@@ -469,7 +469,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   }
   if (p->total_q > 0) {
     prof_begin(BSA_KERNEL_BWD_DQ, s);
-    e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * (p->block_x / 128)), s);
+    e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128)), s);
     prof_end(BSA_KERNEL_BWD_DQ, s);
   }
   return from_hip(e);

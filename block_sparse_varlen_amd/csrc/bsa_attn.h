@@ -9,7 +9,7 @@
 namespace bsa {
 
 constexpr int KT = 64;   // keys per sub-tile of the Q-major kernels
-constexpr int QT = 128;  // query rows per Q-major work item (4 waves x 32); block_x is a multiple
+constexpr int QT = 128;  // query rows per Q-major work item (4 waves x 32)
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  xcd_item maps dispatch index `bid` to a work item so that every XCD
@@ -23,7 +23,8 @@ __device__ __forceinline__ int64_t xcd_item(int64_t bid) {
   return (k / XCD_SEG) * (NUM_XCD * XCD_SEG) + x * XCD_SEG + (k % XCD_SEG);
 }
 
-// A Q-major work item: a 128-row slice of one q-block of one q-head.
+// A Q-major work item: a slice of at most 128 rows of one q-block of one
+// q-head (block_x is a multiple of 64: ceil(block_x / 128) slices).
 struct QItem {
   int r;        // CSR row
   int h, g;     // q-head, kv-head
@@ -34,14 +35,14 @@ struct QItem {
   int nrows;    // valid query rows in the item
 };
 
-// item = (slot * heads_per_row + j) * (block_x / 128) + slice; slot indexes
-// the longest-first row order.  Returns false past the last item and for a
-// slice that starts past the sequence end (nothing to do).
+// item = (slot * heads_per_row + j) * slices + slice; slot indexes the
+// longest-first row order.  Returns false past the last item and for a slice
+// that starts past the sequence end (nothing to do).
 __device__ __forceinline__ bool decode_qitem(int64_t item, const int32_t* hdr, const int32_t* work,
                                              const int32_t* qb_seq, const int32_t* qbase, const SeqArgs& seq,
                                              int heads_per_row, int group, QItem& it) {
   const int R = ldu(hdr, H_R);
-  const int slices = seq.bx / QT;
+  const int slices = (seq.bx + QT - 1) / QT;
   if (item >= (int64_t)R * heads_per_row * slices) return false;
   const int64_t ritem = item / slices;
   const int slice = (int)(item - ritem * slices);
@@ -59,7 +60,7 @@ __device__ __forceinline__ bool decode_qitem(int64_t item, const int32_t* hdr, c
   it.sq = (int)(ldu(seq.cu_q, it.b + 1) - it.q0);
   it.skv = seq.seqused_kv ? ldu(seq.seqused_kv, it.b) : (int)(ldu(seq.cu_kv, it.b + 1) - ldu(seq.cu_kv, it.b));
   it.row_lo = it.qb * seq.bx + slice * QT;
-  it.nrows = min(QT, it.sq - it.row_lo);
+  it.nrows = min(min(QT, seq.bx - slice * QT), it.sq - it.row_lo);
   return it.nrows > 0;
 }
 

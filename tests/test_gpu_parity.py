@@ -53,6 +53,10 @@ def fwd_cases():
         "mask_bx256_causal": R(111, lens_q=[700, 300], N1=2, D=128, kind="mask", bx=256, causal=True),
         "idx_bx512_gqa_paged_by256": R(112, lens_q=[1100, 520], lens_kv=[900, 1300], N1=4, N2=2, D=128,
                                        kind="idx", sparse_heads=2, bx=512, by=256, paged=True, page_size=256),
+        # q-blocks of 64 and 192 rows (work items of 64 rows)
+        "sabi_bx64_causal": R(113, lens_q=[300, 170], N1=2, D=128, kind="sabi", bx=64, causal=True),
+        "mask_bx192_f16_d64": R(114, lens_q=[500, 391], lens_kv=[450, 600], N1=2, D=64, dtype="f16",
+                                kind="mask", bx=192),
     }
 
 
@@ -82,6 +86,10 @@ def bwd_cases():
                                    causal=True),
         "sabi_bx512_by256_causal": R(211, lens_q=[1100, 520], lens_kv=[1300, 900], N1=2, D=128,
                                      kind="sabi", bx=512, by=256, causal=True),
+        "idx_bx64_gqa_causal": R(212, lens_q=[300, 170], N1=4, N2=2, D=128, kind="idx", sparse_heads=2,
+                                 bx=64, causal=True),
+        "mask_bx192_paged": R(213, lens_q=[500, 391], lens_kv=[450, 600], N1=2, D=128, kind="mask", bx=192,
+                              paged=True),
     }
 
 
