@@ -294,38 +294,13 @@ __device__ __forceinline__ int64_t kv_tile_offset(const SeqArgs& seq, const int3
 
 // Walk over the T-key sub-tiles of a CSR row: blocks cols[e0..e1), each cut
 // into by / T sub-tiles, keeping those whose first key is below `kend` (the
-// key bound of the item: Skv, or the causal limit of its last row + 1).  Every
-// listed block starts below kend, so only the later sub-tiles are tested.
-template <int T = KT>
-struct SubTileWalk {
-  const int32_t* cols;
-  int e, e1, s, nsub, by, kend;
-  __device__ __forceinline__ void init(const int32_t* c, int e0, int e_end, int by_, int kend_) {
-    cols = c;
-    e = e0;
-    e1 = e_end;
-    s = 0;
-    by = by_;
-    nsub = by_ / T;
-    kend = kend_;
-  }
-  __device__ __forceinline__ bool valid() const { return e < e1; }
-  __device__ __forceinline__ int key() const { return ldu(cols, e) * by + s * T; }
-  __device__ __forceinline__ void next() {
-    ++s;
-    if (s >= nsub || ldu(cols, e) * by + s * T >= kend) {
-      ++e;
-      s = 0;
-    }
-  }
-};
-
-// The same walk with the row's block list held in a VGPR (lane l holds entry
-// base + l), so handing out a sub-tile is a lane read instead of a scalar
-// memory round trip on the critical path of the tile copies.  Rows of more
-// than 64 entries reload the register per 64 entries and wait for that load
-// on the spot (rare), which leaves the compiler no pending load of it to wait
-// for elsewhere -- such a wait would also drain the tile copies in flight.
+// key bound of the item: Skv, or the causal limit of its last row + 1).  The
+// row's block list is held in a VGPR (lane l holds entry base + l), so
+// handing out a sub-tile is a lane read instead of a scalar memory round trip
+// on the critical path of the tile copies.  Rows of more than 64 entries
+// reload the register per 64 entries and wait for that load on the spot
+// (rare), which leaves the compiler no pending load of it to wait for
+// elsewhere -- such a wait would also drain the tile copies in flight.
 template <int T = KT>
 struct RegTileWalk {
   const int32_t* cols;

@@ -57,6 +57,8 @@ def fwd_cases():
         "sabi_bx64_causal": R(113, lens_q=[300, 170], N1=2, D=128, kind="sabi", bx=64, causal=True),
         "mask_bx192_f16_d64": R(114, lens_q=[500, 391], lens_kv=[450, 600], N1=2, D=64, dtype="f16",
                                 kind="mask", bx=192),
+        # rows of more than 64 visited blocks (the block list is read 64 entries at a time)
+        "none_by64_long_rows": R(115, lens_q=[256, 130], lens_kv=[4500, 9000], N1=2, D=64, kind="none", by=64),
     }
 
 
@@ -90,6 +92,8 @@ def bwd_cases():
                                  bx=64, causal=True),
         "mask_bx192_paged": R(213, lens_q=[500, 391], lens_kv=[450, 600], N1=2, D=128, kind="mask", bx=192,
                               paged=True),
+        "mask_long_rows_by128": R(214, lens_q=[200, 130], lens_kv=[9000, 12000], N1=2, D=64, kind="mask",
+                                  density=0.9),
     }
 
 
