@@ -295,7 +295,7 @@ def _cfg_bwd(n):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("n", [1, 2, 4, 5])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_bwd_config(n):
     case = _cfg_bwd(n)
     say(f"config {n}: bwd on GPU")
