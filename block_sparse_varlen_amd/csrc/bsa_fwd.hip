@@ -7,13 +7,13 @@
 // path) and the log-sum-exp produced in the same pass (BlitzSparseAttention
 // page, "softmax_lse output").
 //
-// One workgroup (4 waves) per work item = one 128-row q-block of one q-head,
-// taken longest-first from the index preprocessor's order.  Wave w owns query
-// rows 32w .. 32w+31 and keeps its Q rows in registers.  The kernel walks the
-// item's selected KV blocks in 64-key sub-tiles: K and V are staged through
-// registers into double-buffered LDS (16-byte global loads, the next
-// sub-tile's loads in flight while the current one is computed), then each
-// wave computes
+// One workgroup (4 waves) per work item = up to 128 rows of one q-block of
+// one q-head, taken longest-first from the index preprocessor's order.  Wave w
+// owns query rows 32w .. 32w+31 and keeps its Q rows in registers.  The kernel
+// walks the item's selected KV blocks in 64-key sub-tiles: K and V are copied
+// straight from global memory into double-buffered LDS (direct-to-LDS loads,
+// the next sub-tile's copies in flight while the current one is computed),
+// then each wave computes
 //   S^T = K Q^T           (MFMA 32x32x16, K read row-major from LDS)
 //   online softmax        (each lane owns one query row: in-register max/sum,
 //                          one cross-half exchange)

@@ -39,7 +39,8 @@
  * Ownership.  Every pointer argument of stage 2 is caller-owned device
  * memory (except the descriptor, a host pointer).  The library never
  * allocates, frees or synchronizes; outputs are fully overwritten (no
- * pre-zeroing needed) and must not alias inputs or the workspace; workspace
+ * pre-zeroing needed; for paged dK/dV see bsa_bwd) and must not alias inputs
+ * or the workspace; workspace
  * contents are undefined on entry and exit.  Calls on different streams with
  * different workspaces may run concurrently.
  *
@@ -105,8 +106,8 @@ typedef struct bsa_problem {
   int64_t total_kv;          /* T_kv rows of k/v (TND) or number of pages (paged) */
   int32_t max_seqlen_q;      /* upper bound on every Sq_b */
   int32_t max_seqlen_kv;     /* upper bound on every Skv_b */
-  int32_t block_x;           /* q rows per selection block; 128 */
-  int32_t block_y;           /* keys per selection block; multiple of 64, <= 4096 */
+  int32_t block_x;           /* q rows per selection block; multiple of 64, <= 4096 */
+  int32_t block_y;           /* keys per selection block; multiple of 64 (of 128 for bsa_bwd), <= 4096 */
   int32_t sparse_kind;       /* BSA_SPARSE_* */
   int32_t sparse_heads;      /* Hs: N1 (pattern per q-head) or N2 (shared by a GQA group) */
   int32_t sparse_rows;       /* row dimension of the selection tensor (see BSA_SPARSE_*) */
