@@ -235,6 +235,44 @@ def test_bwd_deterministic():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# ------------------------------------------------------------ guard regions --
+
+def _guarded(like, guard, fill):
+    """A buffer of `like`'s shape and dtype inside a larger one whose `guard`
+    leading and trailing elements hold `fill`."""
+    n = like.numel()
+    big = torch.full((n + 2 * guard,), fill, dtype=like.dtype, device=like.device)
+    return big, big[guard:guard + n].view(like.shape)
+
+
+@pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_paged_causal_gqa", "mask_bx192_paged",
+                                  "mask_f16_d64_ragged_empty_seq"])
+def test_no_writes_outside_buffers(name):
+    """Outputs and workspace sit between guard regions (NaN, or a byte pattern
+    for the workspace); a forward and a backward call leave every guard as it
+    was and still match the oracle."""
+    case = BWD[name]
+    say(f"guards {name}")
+    dc = DeviceCase(case, with_bwd=True)
+    G = 8192
+    guards = {}
+    for attr in ("out", "lse", "dq", "dk", "dv"):
+        big, view = _guarded(getattr(dc, attr), G, float("nan"))
+        guards[attr] = big
+        setattr(dc, attr, view)
+    wbig, dc.ws = _guarded(dc.ws, G, 0xA5)
+    nan_fill(dc.out, dc.lse)
+    dc.fwd()
+    nan_fill(dc.dq, dc.dk, dc.dv)
+    dc.bwd()
+    torch.cuda.synchronize()
+    for attr, big in guards.items():
+        assert torch.isnan(big[:G]).all() and torch.isnan(big[-G:]).all(), f"{attr}: write outside the buffer"
+    assert (wbig[:G] == 0xA5).all() and (wbig[-G:] == 0xA5).all(), "workspace: write outside the buffer"
+    check_fwd(case, dc, tag=name)
+    check_bwd(case, dc, tag=name)
+
+
 # ---------------------------------------------------- benchmark workloads --
 
 @functools.lru_cache(maxsize=1)
