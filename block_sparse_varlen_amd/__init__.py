@@ -33,6 +33,7 @@ BSA_DTYPE_F16, BSA_DTYPE_BF16 = 1, 2
 BSA_SPARSE_NONE, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_SABI_U16, BSA_SPARSE_IDX_I32 = 0, 1, 2, 3
 BSA_MASK_NONE, BSA_MASK_CAUSAL = 0, 1
 BSA_KV_TND, BSA_KV_PAGED = 0, 1
+BSA_FLAG_INDEX_BUILT = 1
 (BSA_KERNEL_INDEX, BSA_KERNEL_FWD, BSA_KERNEL_BWD_PRE, BSA_KERNEL_BWD_DKDV, BSA_KERNEL_BWD_DQ) = range(5)
 KERNEL_NAMES = {0: "index", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq"}
 

@@ -44,7 +44,7 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
     if (p->page_stride < (int64_t)p->page_size * row || p->page_stride % row != 0) return BSA_ERR_PARAM_INVALID;
   }
   if (!(p->scale >= 0.0) || !std::isfinite(p->scale)) return BSA_ERR_PARAM_INVALID;
-  if (p->flags != 0 || p->reserved != 0) return BSA_ERR_PARAM_INVALID;
+  if ((p->flags & ~(uint32_t)BSA_FLAG_INDEX_BUILT) != 0 || p->reserved != 0) return BSA_ERR_PARAM_INVALID;
   // valid descriptors without a compiled variant
   if (p->block_x % 64 != 0 || p->block_x > 4096) return BSA_ERR_INNER;
   if (p->block_y % 64 != 0 || p->block_y > 4096) return BSA_ERR_INNER;
@@ -106,7 +106,10 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   L.row_cnt = take((size_t)b.rbar * 4);
   L.row_ptr = take((size_t)(b.rbar + 1) * 4);
   L.cols = take((size_t)b.nnzbar * 4);
-  const int64_t nsort = std::max<int64_t>(b.rbar, with_csc ? b.kvbar : 0);
+  // sized for both sorts whatever with_csc is, so the forward products sit at
+  // the same offsets in the forward and the backward layout (an index built
+  // for the backward pass serves a forward call too)
+  const int64_t nsort = std::max<int64_t>(b.rbar, b.kvbar);
   L.key0 = take((size_t)nsort * 4);
   L.val0 = take((size_t)nsort * 4);
   L.key1 = take((size_t)nsort * 4);
@@ -355,10 +358,13 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
   const IndexPtrs ip = make_ptrs(workspace, L, false);
   const int group = p->num_heads_q / p->num_heads_kv;
   const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
-  prof_begin(BSA_KERNEL_INDEX, s);
-  hipError_t e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, false, s);
-  prof_end(BSA_KERNEL_INDEX, s);
-  if (e != hipSuccess) return BSA_ERR_RUNTIME;
+  hipError_t e = hipSuccess;
+  if (!(p->flags & BSA_FLAG_INDEX_BUILT)) {
+    prof_begin(BSA_KERNEL_INDEX, s);
+    e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, false, s);
+    prof_end(BSA_KERNEL_INDEX, s);
+    if (e != hipSuccess) return BSA_ERR_RUNTIME;
+  }
 
   FwdArgs a{};
   a.q = q;
@@ -413,10 +419,13 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   const IndexPtrs ip = make_ptrs(workspace, L, true);
   const int group = p->num_heads_q / p->num_heads_kv;
   const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
-  prof_begin(BSA_KERNEL_INDEX, s);
-  hipError_t e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, true, s);
-  prof_end(BSA_KERNEL_INDEX, s);
-  if (e != hipSuccess) return BSA_ERR_RUNTIME;
+  hipError_t e = hipSuccess;
+  if (!(p->flags & BSA_FLAG_INDEX_BUILT)) {
+    prof_begin(BSA_KERNEL_INDEX, s);
+    e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, true, s);
+    prof_end(BSA_KERNEL_INDEX, s);
+    if (e != hipSuccess) return BSA_ERR_RUNTIME;
+  }
 
   float* dl = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.dl);
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse2);

@@ -5,12 +5,14 @@ No attention arithmetic happens here.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import torch
 
 from . import (
     BSA_DTYPE_BF16, BSA_DTYPE_F16, BSA_KV_PAGED, BSA_KV_TND, BSA_MASK_CAUSAL, BSA_MASK_NONE,
-    BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_IDX_I32, BSA_SPARSE_NONE, BSA_SPARSE_SABI_U16,
+    BSA_FLAG_INDEX_BUILT, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_IDX_I32, BSA_SPARSE_NONE, BSA_SPARSE_SABI_U16,
     bsa_build_index, bsa_bwd, bsa_fwd, bsa_get_workspace_size, bsa_index_view, problem,
 )
 
@@ -53,6 +55,10 @@ def _dev(a, device, dtype=None):
     return t.to(device)
 
 
+def ctypes_copy(dst, src):
+    ctypes.memmove(ctypes.byref(dst), ctypes.byref(src), ctypes.sizeof(src))
+
+
 class DeviceCase:
     """Inputs resident on the GPU plus output and workspace buffers."""
 
@@ -92,14 +98,29 @@ class DeviceCase:
             self.dk = torch.empty_like(self.k)
             self.dv = torch.empty_like(self.v)
 
-    def fwd(self, stream=None):
-        bsa_fwd(self.p, self.q, self.k, self.v, self.cu_q, self.cu_kv, self.seqused_kv, self.sparse, self.count,
-                self.block_table, self.out, self.lse, self.ws, None, stream)
+    def _prob(self, prebuilt: bool):
+        if not prebuilt:
+            return self.p
+        p = type(self.p)()
+        ctypes_copy(p, self.p)
+        p.flags |= BSA_FLAG_INDEX_BUILT
+        return p
 
-    def bwd(self, stream=None):
-        bsa_bwd(self.p, self.q, self.k, self.v, self.out, self.dout, self.lse, self.cu_q, self.cu_kv,
-                self.seqused_kv, self.sparse, self.count, self.block_table, self.dq, self.dk, self.dv, self.ws,
-                None, stream)
+    def build_index(self, with_csc: bool, stream=None):
+        """Enqueues the block index build into the workspace (no readback)."""
+        bsa_build_index(self.p, self.cu_q, self.cu_kv, self.seqused_kv, self.sparse, self.count, with_csc,
+                        self.ws, None, stream)
+
+    def fwd(self, stream=None, prebuilt: bool = False):
+        """``prebuilt``: use the index build_index() left in the workspace."""
+        bsa_fwd(self._prob(prebuilt), self.q, self.k, self.v, self.cu_q, self.cu_kv, self.seqused_kv, self.sparse,
+                self.count, self.block_table, self.out, self.lse, self.ws, None, stream)
+
+    def bwd(self, stream=None, prebuilt: bool = False):
+        """``prebuilt``: use the index build_index(with_csc=True) left in the workspace."""
+        bsa_bwd(self._prob(prebuilt), self.q, self.k, self.v, self.out, self.dout, self.lse, self.cu_q,
+                self.cu_kv, self.seqused_kv, self.sparse, self.count, self.block_table, self.dq, self.dk, self.dv,
+                self.ws, None, stream)
 
     def index(self, with_csc: bool):
         """Builds the block index and returns its products as numpy arrays."""

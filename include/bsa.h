@@ -95,6 +95,17 @@ enum { BSA_MASK_NONE = 0, BSA_MASK_CAUSAL = 1 };
    (GenericBlockSparseAttention page, "Paged Attention", PA_BBND). */
 enum { BSA_KV_TND = 0, BSA_KV_PAGED = 1 };
 
+/* Call flags (bsa_problem_t.flags).
+ * BSA_FLAG_INDEX_BUILT: the workspace already holds the block index of this
+ *   problem and selection, built by bsa_build_index() into it (with_csc != 0
+ *   for bsa_bwd) and not overwritten since, so bsa_fwd / bsa_bwd skip
+ *   rebuilding it -- GenericBlockSparseAttention's metadata operator, whose
+ *   output the main operator consumes; as there, an index that does not match
+ *   the call (other problem, selection or sequence lengths) is undefined
+ *   behaviour.  A training step can build the index once and run both passes
+ *   on it.  The workspace size rules are unchanged. */
+enum { BSA_FLAG_INDEX_BUILT = 1u };
+
 typedef struct bsa_problem {
   uint32_t struct_size;      /* sizeof(bsa_problem_t) */
   int32_t dtype;             /* BSA_DTYPE_*: q, k, v, out, dout, dq, dk, dv */
@@ -118,7 +129,7 @@ typedef struct bsa_problem {
   int32_t max_pages_per_seq; /* paged: second dimension of block_table */
   int64_t page_stride;       /* paged: elements between pages, >= page_size*N2*D, multiple of N2*D */
   double scale;              /* > 0, or 0 for 1/sqrt(D); applied rounded to fp32 */
-  uint32_t flags;            /* reserved, must be 0 */
+  uint32_t flags;            /* BSA_FLAG_* bits, others must be 0 */
   uint32_t reserved;         /* must be 0 */
 } bsa_problem_t;
 

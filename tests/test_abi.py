@@ -75,7 +75,8 @@ def test_workspace_size_ok():
     (dict(mask_type=2), bsa.BSA_ERR_PARAM_INVALID),
     (dict(scale=-1.0), bsa.BSA_ERR_PARAM_INVALID),
     (dict(scale=float("nan")), bsa.BSA_ERR_PARAM_INVALID),
-    (dict(flags=1), bsa.BSA_ERR_PARAM_INVALID),
+    (dict(flags=2), bsa.BSA_ERR_PARAM_INVALID),  # unknown flag bit
+    (dict(flags=bsa.BSA_FLAG_INDEX_BUILT), bsa.BSA_OK),
     (dict(kv_layout=bsa.BSA_KV_PAGED, page_size=128, max_pages_per_seq=1, page_stride=128 * 2 * 128),
      bsa.BSA_ERR_PARAM_INVALID),  # too few pages per sequence for max_seqlen_kv
     (dict(kv_layout=bsa.BSA_KV_PAGED, page_size=128, max_pages_per_seq=4, page_stride=100),

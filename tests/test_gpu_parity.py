@@ -235,6 +235,32 @@ def test_bwd_deterministic():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# ------------------------------------------------------- prebuilt index --
+
+@pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_paged_causal_gqa", "sabi_bx512_by256_causal"])
+def test_prebuilt_index(name):
+    """bsa_build_index (with the transposed lists) once, then bsa_fwd and
+    bsa_bwd with BSA_FLAG_INDEX_BUILT: same results as self-indexing calls,
+    bit for bit."""
+    case = BWD[name]
+    say(f"prebuilt {name}")
+    dc = DeviceCase(case, with_bwd=True)
+    dc.fwd()
+    dc.bwd()
+    ref = [t.clone() for t in (dc.out, dc.lse, dc.dq, dc.dk, dc.dv)]
+    nan_fill(dc.out, dc.lse, dc.dq, dc.dk, dc.dv)
+    dc.ws.fill_(0xFF)
+    dc.build_index(True)
+    dc.fwd(prebuilt=True)
+    dc.bwd(prebuilt=True)
+    torch.cuda.synchronize()
+    val = torch.from_numpy(kv_valid(case)).to(dc.dk.device)
+    for a, b, nm in zip(ref, (dc.out, dc.lse, dc.dq, dc.dk, dc.dv), ("out", "lse", "dq", "dk", "dv")):
+        if nm in ("dk", "dv"):
+            a, b = a[val], b[val]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), nm
+
+
 # ------------------------------------------------------------ guard regions --
 
 def _guarded(like, guard, fill):
