@@ -23,7 +23,9 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ------------------------------------------------------------- D = dO.O --
-// One 16-byte chunk per thread, D/8 threads per (token, head) row.
+// One 16-byte chunk per thread, D/8 threads per (token, head) row.  D is
+// stored negated: the dP accumulators of the other two kernels start from
+// -D, so their MFMAs produce dP - D directly.
 template <typename MF, int D>
 __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
   constexpr int CH = D / 8;
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 #pragma unroll
   for (int m = CH / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if (row < a.rows && c == 0) {
-    a.dl[row] = acc;
+    a.ndl[row] = -acc;
     a.lse2[row] = a.lse[row] * LOG2E;
   }
 }
@@ -50,6 +52,8 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 //   S^T = K Q^T, dP^T = V dO^T            (K, V row-major from LDS)
 //   P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T o (dP^T - D)
 //   dQ^T += K^T dS^T                       (K^T via LDS transpose loads)
+// The dP^T accumulator starts from -D (a loop-invariant register tile), and
+// key masks run only on sub-tiles that reach past Skv or the causal limit.
 
 template <typename MF, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
@@ -82,7 +86,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     df[kk] = row_ok ? gload16(reinterpret_cast<const uint16_t*>(a.dout) + qoffs + 16 * kk) : zero_u4();
   }
   const float lse2 = row_ok ? a.lse[tok * a.n1 + it.h] * LOG2E : INFINITY;
-  const float dl = row_ok ? a.dl[tok * a.n1 + it.h] : 0.f;
+  // -D of this lane's row in every element: the start value of each dP^T tile
+  f32x16_t ndt;
+  {
+    const float nd = row_ok ? a.ndl[tok * a.n1 + it.h] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndt[i] = nd;
+  }
 
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
@@ -123,9 +133,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     if (more) issue(stage ^ 1, std::false_type{});
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
+    const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // 32-key halves of the sub-tile
-      f32x16_t s = zero16(), dp = zero16();
+      f32x16_t s = zero16(), dp = ndt;
       // step i: kk = i / 2; even = S^T (K rows), odd = dP^T (V rows)
       mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? vl : kl, of, 32 * t, i >> 1); },
                                 [&](int i, const u32x4_t& op) {
@@ -135,12 +146,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
                                     s = MF::mfma(op, qf[i >> 1], s);
                                 });
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        float p = fast_exp2(fmaf(s[i], c2, -lse2));
-        if (key > lim) p = 0.f;
-        s[i] = p * (dp[i] - dl);  // dS^T
+      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], c2, -lse2));
+      if (edge) {  // keys past Skv or above this row's causal limit
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (key > lim) s[i] = 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] *= dp[i];  // dS^T = P^T o (dP^T - D)
       const u32x4_t db0 = pack8<MF>(s, 0), db1 = pack8<MF>(s, 8);
       // step i: kc = 2 t + i / NMT, mt = i % NMT
       mfma_pipeline<2 * NMT, 4>(
@@ -325,8 +340,8 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     dma.issue(st, qp + off, nvalid);
     dma.issue(st + TILE, dop + off, nvalid);
     float* stat = reinterpret_cast<float*>(st + 2 * TILE);
-    // lse (wave 0) and D (wave 1) of the tile's rows
-    dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.dl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    // lse (wave 0) and -D (wave 1) of the tile's rows
+    dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.ndl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     ld.next();
   };
 
@@ -344,18 +359,28 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     char* ql = smem + stage * STAGE;
     char* dl_ = ql + TILE;
     const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
-    const float* dll = lsel + QS;
+    const float* ndll = lsel + QS;
 
     // Rows past the sequence end, or keys above some row's causal limit,
     // need masks; every other tile takes the mask-free path.
     const bool masked = nrows < QS || (CAUSAL && key_lo + 127 > r0 + qoff);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
+      // dP starts from -D of each element's row, so the MFMAs leave dP - D
       f32x16_t s[2], dp[2];
+      {
+        f32x16_t ndt;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        s[n] = zero16();
-        dp[n] = zero16();
+        for (int ig = 0; ig < 4; ++ig) {
+          const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(ndll + 32 * h + 8 * ig + 4 * (lane >> 5));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ndt[4 * ig + j] = __uint_as_float(d4[j]);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          s[n] = zero16();
+          dp[n] = ndt;
+        }
       }
       // S, dP of rows 32 h .. + 31: each Q / dO operand read feeds both key tiles
       mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * h, i >> 1); },
@@ -374,7 +399,6 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
       for (int ig = 0; ig < 4; ++ig) {
         const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
         const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(lsel + rl);
-        const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(dll + rl);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * ig + j;
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
           for (int n = 0; n < 2; ++n) {
             const float p = fast_exp2(fmaf(s[n][i], c2, -__uint_as_float(l4[j])));
             s[n][i] = p;
-            dp[n][i] = p * (dp[n][i] - __uint_as_float(d4[j]));
+            dp[n][i] *= p;
           }
         }
       }

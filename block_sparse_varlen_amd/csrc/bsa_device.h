@@ -221,15 +221,23 @@ __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// Maximum of the 32 values of two accumulator fragments as a balanced tree.
+__device__ __forceinline__ float max3f(float x, float y, float z) { return fmaxf(fmaxf(x, y), z); }
+// Maximum of the 32 values of two accumulator fragments: a tree of 15
+// three-input maxima (v_max3_f32) and one two-input one.
 __device__ __forceinline__ float max32(const f32x16_t& a, const f32x16_t& b) {
-  float m[8];
+  float v[32], m[12], n[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = fmaxf(fmaxf(a[4 * i], a[4 * i + 1]), fmaxf(a[4 * i + 2], a[4 * i + 3]));
-    m[4 + i] = fmaxf(fmaxf(b[4 * i], b[4 * i + 1]), fmaxf(b[4 * i + 2], b[4 * i + 3]));
+  for (int i = 0; i < 16; ++i) {
+    v[i] = a[i];
+    v[16 + i] = b[i];
   }
-  return fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+#pragma unroll
+  for (int k = 0; k < 10; ++k) m[k] = max3f(v[3 * k], v[3 * k + 1], v[3 * k + 2]);
+  m[10] = v[30];
+  m[11] = v[31];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) n[k] = max3f(m[3 * k], m[3 * k + 1], m[3 * k + 2]);
+  return fmaxf(max3f(n[0], n[1], n[2]), n[3]);
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {

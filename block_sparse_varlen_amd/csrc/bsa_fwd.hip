@@ -150,14 +150,17 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run * c2;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums (short dependency chains)
+    float ps[4];  // independent partial sums (short dependency chains)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(s[t][i], c2, -m_use));
         s[t][i] = p;
-        ps[i & 3] += p;
+        if (t == 0 && i < 4)
+          ps[i] = p;
+        else
+          ps[i & 3] += p;
       }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // ---- O^T += V^T P^T ----
