@@ -226,20 +226,23 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # split fwd / bwd
-    ef = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    fwd_ms = bwd_ms = 0.0
-    for _ in range(args.steps):
-        ef[0].record(stream)
-        fwd_part()
-        ef[1].record(stream)
+    # split: index build, forward call, backward call -- events between the
+    # calls of back-to-back steps, one synchronisation at the end, so no
+    # bracket starts on an idle GPU waiting for its first launch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        if shared:
+            dc.build_index(True)
+        ev[k][1].record(stream)
+        dc.fwd(prebuilt=shared)
+        ev[k][2].record(stream)
         dc.bwd(prebuilt=shared)
-        ef[2].record(stream)
-        torch.cuda.synchronize()
-        fwd_ms += ef[0].elapsed_time(ef[1])
-        bwd_ms += ef[1].elapsed_time(ef[2])
-    fwd_ms /= args.steps
-    bwd_ms /= args.steps
+        ev[k][3].record(stream)
+    torch.cuda.synchronize()
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
 
     # per-kernel durations from events the library records around its launches
     bsa.bsa_profile_enable(True)
@@ -292,6 +295,9 @@ def main():
                    "heads": case.N1, "head_dim": case.D, "block_shape": [case.bx, case.by],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
+        # the block index (built once per step and used by both passes; inside
+        # each call with --self-index) and the two attention calls
+        "index": {"ms": round(idx_ms, 4), "shared": shared},
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
                 "frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": f_fwd},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
