@@ -114,7 +114,8 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   L.val0 = take((size_t)nsort * 4);
   L.key1 = take((size_t)nsort * 4);
   L.val1 = take((size_t)nsort * 4);
-  L.hist = take((size_t)(256 * cdiv64(nsort, 256) + 1) * 4);
+  // one radix sort's histograms, or both work lists' side by side
+  L.hist = take((size_t)(256 * (cdiv64(b.rbar, 256) + cdiv64(b.kvbar, 256)) + 2) * 4);
   L.work = take((size_t)b.rbar * 4);
   if (with_csc) {
     L.col_cnt = take((size_t)b.cbar * 4);

@@ -165,10 +165,17 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
   return nbits;
 }
 
+// Also clears the column counters of the transpose (zero_n entries of col_cnt
+// and col_fill, 0 without it) with a grid-stride loop: the next launches
+// count into them.
 __global__ __launch_bounds__(256) void k_row_count(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t rbar,
-                                                   int words, int cmax) {
+                                                   int words, int cmax, int64_t zero_n) {
   extern __shared__ uint32_t smem_bm[];
   const int wv = threadIdx.x >> 6, lane = lane_id();
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < zero_n; i += (int64_t)gridDim.x * 256) {
+    ip.col_cnt[i] = 0;
+    ip.col_fill[i] = 0;
+  }
   uint32_t* bm = smem_bm + wv * words;
   const int64_t r = (int64_t)blockIdx.x * 4 + wv;
   const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB];
@@ -183,7 +190,10 @@ __global__ __launch_bounds__(256) void k_row_count(SeqArgs seq, SelArgs sel, Ind
   }
 }
 
-__global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t rbar, int words) {
+// With count_cols, also counts each visited block into its column of the
+// transpose (col_cnt, cleared by k_row_count).
+__global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t rbar, int words,
+                                                  int count_cols) {
   extern __shared__ uint32_t smem_bm[];
   const int wv = threadIdx.x >> 6, lane = lane_id();
   uint32_t* bm = smem_bm + wv * words;
@@ -191,6 +201,12 @@ __global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, Inde
   const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB];
   const int nbits = row_bitmap(bm, seq, sel, ip, r < rbar ? (int)r : R, R, TQB);
   if (r >= R) return;
+  int cbase = -1;  // column of KV block 0 of this row's sequence and head
+  if (count_cols) {
+    const int hs = (int)r / TQB;
+    const int b = ip.qb_seq[(int)r - hs * TQB];
+    cbase = hs * ip.hdr[H_TKB] + ip.kbase[b];
+  }
   const int nwords = (nbits + 31) >> 5;
   int pos = ip.row_ptr[r];
   for (int c = 0; c < nwords; c += 64) {
@@ -202,6 +218,7 @@ __global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, Inde
     while (word) {
       const int bit = __ffs(word) - 1;
       ip.cols[o++] = w * 32 + bit;
+      if (cbase >= 0) atomicAdd(&ip.col_cnt[cbase + w * 32 + bit], 1);
       word &= word - 1;
     }
     pos += __shfl(inc, 63, 64);
@@ -210,8 +227,9 @@ __global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, Inde
 
 // --------------------------------------------------------- exclusive scan --
 // out[0..n) = exclusive prefix sums of in[0..n), out[n] = total; also copies
-// the total to *total_out when given.  One block of 1024 threads.
-__global__ __launch_bounds__(1024) void k_scan_excl(const int32_t* in, int32_t* out, int64_t n, int32_t* total_out) {
+// the total to *total_out when given.  One block of 1024 threads; in and out
+// may be the same array.
+__device__ void scan_excl(const int32_t* in, int32_t* out, int64_t n, int32_t* total_out) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
   int carry = 0;
@@ -239,6 +257,16 @@ __global__ __launch_bounds__(1024) void k_scan_excl(const int32_t* in, int32_t* 
     out[n] = carry;
     if (total_out) *total_out = carry;
   }
+}
+
+__global__ __launch_bounds__(1024) void k_scan_excl(const int32_t* in, int32_t* out, int64_t n, int32_t* total_out) {
+  scan_excl(in, out, n, total_out);
+}
+// The same for two independent arrays in one launch.
+__global__ __launch_bounds__(1024) void k_scan_excl2(int32_t* a, int64_t na, int32_t* b, int64_t nb) {
+  scan_excl(a, a, na, nullptr);
+  __syncthreads();
+  scan_excl(b, b, nb, nullptr);
 }
 
 // ---------------------------------------------------- stable radix sort ----
@@ -291,6 +319,64 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const int32_t* key_in, co
   }
 }
 
+// Both single-pass sorts of the index (rows, dK/dV items) in one launch per
+// step: blocks [0, nba) take sort A, the rest sort B.
+struct SortSeg {
+  const int32_t* key;
+  const int32_t* val;
+  int64_t n;
+  int32_t* hist;  // [256 * nb + 1]
+  int nb;
+  int32_t* dst;
+};
+
+__global__ __launch_bounds__(256) void k_radix_hist2(SortSeg a, SortSeg b) {
+  const bool in_a = (int)blockIdx.x < a.nb;
+  const SortSeg& g = in_a ? a : b;
+  const int blk = in_a ? (int)blockIdx.x : (int)blockIdx.x - a.nb;
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blk * 256 + tid;
+  if (i < g.n) atomicAdd(&h[g.key[i] & 255], 1);
+  __syncthreads();
+  g.hist[(int64_t)tid * g.nb + blk] = h[tid];
+}
+
+__global__ __launch_bounds__(256) void k_radix_scatter2(SortSeg a, SortSeg b) {
+  const bool in_a = (int)blockIdx.x < a.nb;
+  const SortSeg& g = in_a ? a : b;
+  const int blk = in_a ? (int)blockIdx.x : (int)blockIdx.x - a.nb;
+  __shared__ int cnt[4][256];
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  for (int e = tid; e < 1024; e += 256) cnt[e >> 8][e & 255] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blk * 256 + tid;
+  const bool valid = i < g.n;
+  int val = 0, d = 0;
+  if (valid) {
+    val = g.val[i];
+    d = g.key[i] & 255;
+  }
+  uint64_t eq = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t m = __ballot((d >> bit) & 1);
+    eq &= ((d >> bit) & 1) ? m : ~m;
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  const int rank_w = __popcll(eq & lt);
+  const bool leader = valid && ((eq >> lane) == 1ull);
+  if (leader) cnt[wv][d] = __popcll(eq);
+  __syncthreads();
+  if (valid) {
+    int r = rank_w;
+    for (int w = 0; w < wv; ++w) r += cnt[w][d];
+    g.dst[g.hist[(int64_t)d * g.nb + blk] + r] = val;
+  }
+}
+
 // ------------------------------------------------------------- transpose --
 __device__ __forceinline__ void row_coords(const IndexPtrs& ip, int r, int TQB, int& hs, int& b, int& qb) {
   hs = r / TQB;
@@ -326,7 +412,11 @@ __global__ __launch_bounds__(256) void k_col_fill(IndexPtrs ip, int64_t rbar) {
 }
 
 // Puts each column's q-block list in ascending order (one wave per column).
-__global__ __launch_bounds__(256) void k_col_sort(IndexPtrs ip, int64_t cbar, int words, int bx) {
+// With kv_key set (one sparse head per KV head, so dK/dV item i is column i),
+// also writes the items' sort keys: kvkey_max - load, kvkey_max + 1 past the
+// last item.
+__global__ __launch_bounds__(256) void k_col_sort(IndexPtrs ip, int64_t cbar, int words, int bx, int32_t* kv_key,
+                                                  int32_t* kv_val, int kvkey_max) {
   extern __shared__ uint32_t smem_bm[];
   const int wv = threadIdx.x >> 6, lane = lane_id();
   uint32_t* bm = smem_bm + wv * words;
@@ -339,6 +429,10 @@ __global__ __launch_bounds__(256) void k_col_sort(IndexPtrs ip, int64_t cbar, in
     nqb = cdiv(ip.sq[b], bx);
     p0 = ip.col_ptr[c];
     p1 = ip.col_ptr[c + 1];
+  }
+  if (kv_key && c < cbar && lane == 0) {
+    kv_key[c] = c < C ? kvkey_max - (p1 - p0) : kvkey_max + 1;
+    kv_val[c] = (int)c;
   }
   const int nwords = (nqb + 31) >> 5;
   for (int w = lane; w < nwords; w += 64) bm[w] = 0;
@@ -367,7 +461,7 @@ __global__ __launch_bounds__(256) void k_col_sort(IndexPtrs ip, int64_t cbar, in
 // Sort keys of the dK/dV items: item i = g * TKB + kg, load = number of
 // (sparse head of group g, q-block) pairs that reach KV block kg.
 __global__ __launch_bounds__(256) void k_kv_keys(IndexPtrs ip, int64_t kvbar, int hs_total, int n2, int group,
-                                                 int kvkey_max) {
+                                                 int kvkey_max, int32_t* kv_key, int32_t* kv_val) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= kvbar) return;
   const int TKB = ip.hdr[H_TKB];
@@ -383,13 +477,8 @@ __global__ __launch_bounds__(256) void k_kv_keys(IndexPtrs ip, int64_t kvbar, in
     }
     key = kvkey_max - load;
   }
-  ip.key0[i] = key;
-  ip.val0[i] = (int)i;
-}
-
-__global__ __launch_bounds__(256) void k_fill_i32(int32_t* p, int64_t n, int v) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = v;
+  kv_key[i] = key;
+  kv_val[i] = (int)i;
 }
 
 inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -400,44 +489,71 @@ int radix_passes(int64_t maxkey) {
   return bits <= 8 ? 1 : (bits + 7) / 8;
 }
 
-// Sorts (key0, val0)[0..n) and writes the values in key order to `dst`.
-hipError_t radix_sort(const IndexPtrs& ip, int64_t n, int64_t maxkey, int32_t* dst, hipStream_t st) {
+// Sorts (key, val)[0..n) (key1 / val1 hold the intermediate passes) and
+// writes the values in key order to `dst`.
+hipError_t radix_sort(const IndexPtrs& ip, const int32_t* key, const int32_t* val, int64_t n, int64_t maxkey,
+                      int32_t* dst, hipStream_t st) {
   const int nb = (int)blocks_for(n, 256);
   const int passes = radix_passes(maxkey);
-  int32_t *ki = ip.key0, *vi = ip.val0, *ko = ip.key1, *vo = ip.val1;
+  const int32_t *ki = key, *vi = val;
+  int32_t *ko = ip.key1, *vo = ip.val1;
+  int32_t *ko2 = ip.key0, *vo2 = ip.val0;
   for (int p = 0; p < passes; ++p) {
     const bool last = p == passes - 1;
     k_radix_hist<<<nb, 256, 0, st>>>(ki, n, 8 * p, ip.hist, nb);
     k_scan_excl<<<1, 1024, 0, st>>>(ip.hist, ip.hist, (int64_t)nb * 256, nullptr);
     k_radix_scatter<<<nb, 256, 0, st>>>(ki, vi, n, 8 * p, ip.hist, nb, last ? nullptr : ko, last ? dst : vo);
-    int32_t* t = ki; ki = ko; ko = t;
-    t = vi; vi = vo; vo = t;
+    ki = ko;
+    vi = vo;
+    int32_t* t = ko; ko = ko2; ko2 = t;
+    t = vo; vo = vo2; vo2 = t;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Launches: setup, row counts (+ clearing the column counters), row scan,
+// row fill (+ column counts), then either both work lists at the end with one
+// shared hist / scan / scatter launch each (when both sort in one radix pass)
+// or each list with its own passes.
 hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip, int n2,
                         int group, bool with_csc, hipStream_t st) {
+  const bool merged = with_csc && radix_passes((int64_t)bd.cmax + 1) == 1 &&
+                      radix_passes((int64_t)bd.kvkey_max + 1) == 1;
   k_setup<<<1, 256, 0, st>>>(seq, ip, sel.hs, n2);
   const int words = (bd.nkb_max + 31) / 32 > 0 ? (bd.nkb_max + 31) / 32 : 1;
   const size_t lds = 4 * (size_t)words * 4;
   const unsigned rgrid = blocks_for(bd.rbar, 4);
-  k_row_count<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words, bd.cmax);
+  k_row_count<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words, bd.cmax, with_csc ? bd.cbar : 0);
   k_scan_excl<<<1, 1024, 0, st>>>(ip.row_cnt, ip.row_ptr, bd.rbar, ip.hdr + H_NNZ);
-  k_row_fill<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words);
-  hipError_t e = radix_sort(ip, bd.rbar, (int64_t)bd.cmax + 1, ip.work, st);
-  if (e != hipSuccess || !with_csc) return e;
-  k_fill_i32<<<blocks_for(bd.cbar, 256), 256, 0, st>>>(ip.col_cnt, bd.cbar, 0);
-  k_fill_i32<<<blocks_for(bd.cbar, 256), 256, 0, st>>>(ip.col_fill, bd.cbar, 0);
-  k_col_count<<<rgrid, 256, 0, st>>>(ip, bd.rbar);
+  k_row_fill<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words, with_csc ? 1 : 0);
+  hipError_t e = hipSuccess;
+  if (!merged) {
+    e = radix_sort(ip, ip.key0, ip.val0, bd.rbar, (int64_t)bd.cmax + 1, ip.work, st);
+    if (e != hipSuccess || !with_csc) return e;
+  }
+  // dK/dV item keys: key1 / val1 when merged (key0 / val0 still hold the row
+  // keys), else key0 / val0 (the row sort is done)
+  int32_t* kv_key = merged ? ip.key1 : ip.key0;
+  int32_t* kv_val = merged ? ip.val1 : ip.val0;
+  const bool direct = sel.hs == n2;
   k_scan_excl<<<1, 1024, 0, st>>>(ip.col_cnt, ip.col_ptr, bd.cbar, nullptr);
   k_col_fill<<<rgrid, 256, 0, st>>>(ip, bd.rbar);
   const int qwords = (bd.nqb_max + 31) / 32 > 0 ? (bd.nqb_max + 31) / 32 : 1;
-  k_col_sort<<<blocks_for(bd.cbar, 4), 256, 4 * (size_t)qwords * 4, st>>>(ip, bd.cbar, qwords, seq.bx);
-  k_kv_keys<<<blocks_for(bd.kvbar, 256), 256, 0, st>>>(ip, bd.kvbar, sel.hs, n2, group, bd.kvkey_max);
-  return radix_sort(ip, bd.kvbar, (int64_t)bd.kvkey_max + 1, ip.work_kv, st);
+  k_col_sort<<<blocks_for(bd.cbar, 4), 256, 4 * (size_t)qwords * 4, st>>>(
+      ip, bd.cbar, qwords, seq.bx, direct ? kv_key : nullptr, kv_val, bd.kvkey_max);
+  if (!direct)
+    k_kv_keys<<<blocks_for(bd.kvbar, 256), 256, 0, st>>>(ip, bd.kvbar, sel.hs, n2, group, bd.kvkey_max, kv_key,
+                                                         kv_val);
+  if (!merged) return radix_sort(ip, kv_key, kv_val, bd.kvbar, (int64_t)bd.kvkey_max + 1, ip.work_kv, st);
+  const int nba = (int)blocks_for(bd.rbar, 256), nbb = (int)blocks_for(bd.kvbar, 256);
+  const SortSeg sa{ip.key0, ip.val0, bd.rbar, ip.hist, nba, ip.work};
+  const SortSeg sb{ip.key1, ip.val1, bd.kvbar, ip.hist + 256 * (int64_t)nba + 1, nbb, ip.work_kv};
+  k_radix_hist2<<<nba + nbb, 256, 0, st>>>(sa, sb);
+  k_scan_excl2<<<1, 1024, 0, st>>>(sa.hist, 256 * (int64_t)nba, sb.hist, 256 * (int64_t)nbb);
+  k_radix_scatter2<<<nba + nbb, 256, 0, st>>>(sa, sb);
+  return hipGetLastError();
 }
 
 }  // namespace bsa

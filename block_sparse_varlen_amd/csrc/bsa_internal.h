@@ -81,7 +81,7 @@ struct IndexPtrs {
   int32_t* row_ptr;  // [rbar+1]
   int32_t* cols;     // [nnzbar]
   int32_t* key0; int32_t* val0; int32_t* key1; int32_t* val1;  // [max(rbar, kvbar)]
-  int32_t* hist;     // [256 * ceil(max(rbar, kvbar)/256)]
+  int32_t* hist;     // [256 * (ceil(rbar/256) + ceil(kvbar/256)) + 2]
   int32_t* work;     // [rbar]
   int32_t* col_cnt;  // [cbar]
   int32_t* col_ptr;  // [cbar+1]
