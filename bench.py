@@ -162,6 +162,44 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(out, indent=1))
 
 
+def sample_sclk(step, seconds: float = 3.0):
+    """Average graphics clock (MHz) over the XCDs, read with ``amd-smi metric
+    --clock`` from a second thread while ``step`` runs back to back for about
+    ``seconds``; None when the tool is missing or prints no clock."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(0.5)
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock"], capture_output=True, text=True,
+                                   timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            clks = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+            if clks:
+                samples.append(sum(clks) / len(clks))
+            time.sleep(0.1)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            step()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    return (sum(samples) / len(samples), len(samples)) if samples else (None, 0)
+
+
 def main():
     if len(sys.argv) == 4 and sys.argv[1] == "--write-traffic":
         write_traffic(sys.argv[2], sys.argv[3])
@@ -174,6 +212,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5],
                     help="benchmark configuration (default 5, the long-context workload the metric is quoted on)")
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the graphics clock")
     ap.add_argument("--self-index", action="store_true",
                     help="let bsa_fwd and bsa_bwd each build their own block index (no shared build)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -258,6 +297,11 @@ def main():
     bsa.bsa_profile_enable(False)
     print("bench: per-kernel " + json.dumps(per_kernel), file=sys.stderr, flush=True)
 
+    sclk, nsamp = (None, 0)
+    if not args.no_clock:
+        print("bench: sampling the graphics clock", file=sys.stderr, flush=True)
+        sclk, nsamp = sample_sclk(step)
+
     if args.calib_copy:
         x = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
         y = torch.empty_like(x)
@@ -306,6 +350,11 @@ def main():
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        # the clock the steps actually ran at (the peak assumes 2.4 GHz), and the
+        # step's fraction of the peak scaled to that clock
+        "clock": {"sclk_mhz": round(sclk, 1) if sclk else None, "samples": nsamp,
+                  "method": "amd-smi metric --clock, mean over XCDs, while steps run back to back",
+                  "frac_of_peak_at_sclk": round(total_tflops / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4) if sclk else None},
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
