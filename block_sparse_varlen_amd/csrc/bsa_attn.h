@@ -64,45 +64,6 @@ __device__ __forceinline__ bool decode_qitem(int64_t item, const int32_t* hdr, c
   return it.nrows > 0;
 }
 
-// Staging of a [ROWS x D] 16-bit tile whose rows are `row_stride` elements
-// apart: 256 threads, one 16-byte chunk each per pass.  The thread's element
-// offsets inside the tile are fixed per work item; each load takes a uniform
-// base pointer (row 0, column 0 of the tile).
-template <class L, int D, int ROWS>
-struct Stage {
-  static constexpr int CH = D / 8;
-  static constexpr int RPP = 256 / CH;      // rows per pass
-  static constexpr int PASSES = ROWS / RPP;
-  static_assert(ROWS % RPP == 0, "tile rows must fill whole passes");
-  u32x4_t r[PASSES];
-  int toff[PASSES];  // global element offsets of this thread's chunks
-  int loff[PASSES];  // LDS byte offsets of this thread's chunks
-
-  __device__ __forceinline__ void init(int row_stride) {
-    const int c = threadIdx.x % CH;
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      toff[p] = (p * RPP + (int)threadIdx.x / CH) * row_stride + c * 8;
-      loff[p] = L::chunk_off(p * RPP + (int)threadIdx.x / CH, c);
-    }
-  }
-  __device__ __forceinline__ static int row_of(int p) { return p * RPP + (int)threadIdx.x / CH; }
-  // rows >= nvalid are zero-filled
-  __device__ __forceinline__ void load(const uint16_t* base, int nvalid) {
-    if (nvalid >= ROWS) {
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) r[p] = gload16(base + toff[p]);
-    } else {
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) r[p] = row_of(p) < nvalid ? gload16(base + toff[p]) : zero_u4();
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) lds_write16(lds, loff[p], r[p]);
-  }
-};
-
 // s_waitcnt on the vector-memory counter only: wait until at most N of this
 // wave's vector memory operations (loads, and loads into LDS) are in flight.
 template <int N>
@@ -111,18 +72,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (N & 0xF) | ((N >> 4) << 14));
 }
 
-// One wave-wide global -> LDS copy: lane l fetches SIZE (4 or 16) bytes from
-// gbase + off (gbase wave-uniform, off the lane's byte offset) and they land
-// at LDS byte lds + SIZE l.  Issued as inline asm on purpose: when the
-// compiler sees a load that writes LDS it treats it as an access to two
-// memory kinds whose completion order it cannot track, and from then on waits
-// for every outstanding vector-memory and LDS operation (vmcnt(0) /
-// lgkmcnt(0)) before any LDS read -- which would drain the next stage's
-// prefetch in the middle of the current stage.  The kernels synchronise these
-// copies themselves: wait_vmcnt for the issuing wave, then a workgroup
-// barrier before any wave reads the stage.  M0 holds the LDS base (no other
-// code in these kernels uses M0); one wait state separates its write from the
-// copy.
 // LDS byte address of a pointer into __shared__ memory, and a 64-bit value
 // made wave-uniform (readfirstlane returns int: each half is taken as
 // unsigned before widening).
@@ -135,8 +84,18 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
-// The copy itself, from wave-uniform sbase (global byte address) and m0 (LDS
-// byte address) and the lane's byte offset voff.
+// One wave-wide global -> LDS copy: lane l fetches SIZE (4 or 16) bytes from
+// sbase + voff (sbase the wave-uniform global byte address, voff the lane's
+// byte offset) and they land at LDS byte m0 + SIZE l.  Issued as inline asm
+// on purpose: when the compiler sees a load that writes LDS it treats it as
+// an access to two memory kinds whose completion order it cannot track, and
+// from then on waits for every outstanding vector-memory and LDS operation
+// (vmcnt(0) / lgkmcnt(0)) before any LDS read -- which would drain the next
+// stage's prefetch in the middle of the current stage.  The kernels
+// synchronise these copies themselves: wait_vmcnt for the issuing wave, then
+// a workgroup barrier before any wave reads the stage.  M0 holds the LDS base
+// (no other code in these kernels uses M0); one wait state separates its
+// write from the copy.
 template <int SIZE>
 __device__ __forceinline__ void dma_raw(uint64_t sbase, uint32_t voff, uint32_t m0) {
 #pragma clang diagnostic push
@@ -275,21 +234,6 @@ __device__ __forceinline__ void settle_scalar_loads() {
 __device__ __forceinline__ void dma_rows_f32(float* lds, const float* g, int stride, int nvalid) {
   const int r = min(lane_id(), nvalid - 1);
   dma_to_lds<4>(g, 4u * (uint32_t)(r * stride), lds);
-}
-
-// Element offset of key `key0` (row 0 of a sub-tile that stays inside one
-// page) of KV head g in sequence b: packed rows cu_kv[b] + key, or
-// (block_table[b, key / page_size], key % page_size) in the paged layout.
-template <bool PAGED>
-__device__ __forceinline__ int64_t kv_tile_offset(const SeqArgs& seq, const int32_t* block_table, int b, int g,
-                                                  int key0, int n2, int D, int page_size, int max_pages,
-                                                  int64_t page_stride) {
-  if constexpr (PAGED) {
-    const int page = ldu(block_table, (int64_t)b * max_pages + key0 / page_size);
-    return (int64_t)page * page_stride + ((int64_t)(key0 % page_size) * n2 + g) * D;
-  } else {
-    return ((ldu(seq.cu_kv, b) + key0) * n2 + g) * (int64_t)D;
-  }
 }
 
 // Walk over the T-key sub-tiles of a CSR row: blocks cols[e0..e1), each cut
@@ -476,33 +420,6 @@ __device__ __forceinline__ void mfma_pipeline(ReadF read, MfmaF mfma) {
     mfma(i, a);
     __builtin_amdgcn_sched_barrier(0);
   }
-}
-
-// mfma_pipeline with a third callback: extra(i) emits work independent of the
-// pipeline (another tile's softmax) right after step i's MFMAs, so the VALU
-// issues while the matrix core is still busy with them.
-template <int N, int LOOK, class ReadF, class MfmaF, class ExtraF>
-__device__ __forceinline__ void mfma_pipeline_x(ReadF read, MfmaF mfma, ExtraF extra) {
-  u32x4_t ring[LOOK];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < LOOK; ++i) ring[i] = read(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const u32x4_t a = ring[i % LOOK];
-    if (i + LOOK < N) ring[i % LOOK] = read(i + LOOK);
-    mfma(i, a);
-    extra(i);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Maximum of the 16 values of an accumulator fragment as a balanced tree.
-__device__ __forceinline__ float max16(const f32x16_t& a) {
-  float m[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m[i] = fmaxf(fmaxf(a[4 * i], a[4 * i + 1]), fmaxf(a[4 * i + 2], a[4 * i + 3]));
-  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
 }
 
 // Stores a [32 x 32] C fragment holding X^T (rows = feature d, columns =

@@ -39,14 +39,6 @@ struct BF16 {
   static __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
   }
-  // acc = A B (first) or acc += A B with the B operand held in AGPRs and acc in
-  // VGPRs; see mfma_vgpr_done.
-  static __device__ __forceinline__ void mfma_bagpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b, bool first) {
-    if (first)
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
-    else
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-  }
   // Two fp32 values rounded to nearest-even bf16, packed lo | hi << 16.
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     bf16x2_t r;
@@ -66,12 +58,6 @@ struct F16 {
   static __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
   }
-  static __device__ __forceinline__ void mfma_bagpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b, bool first) {
-    if (first)
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
-    else
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-  }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     f16x2_t r;
     r[0] = (_Float16)lo;
@@ -86,15 +72,14 @@ struct F16 {
   }
 };
 
-// mfma_acc pins a long-lived accumulator to the AGPRs, and mfma_bagpr a
-// long-lived B operand, leaving the VGPRs to the operands and to the MFMA
-// results the softmax works on.  The compiler cannot see that the asm is an
+// mfma_acc pins a long-lived accumulator to the AGPRs, leaving the VGPRs to
+// the operands and to the MFMA results the softmax works on.  The compiler cannot see that the asm is an
 // MFMA, so it inserts none of the MFMA wait states; two are covered by hand:
 //  * a VALU write of an operand register (the compiler may stage an operand
 //    through a copy right before the asm) needs 2 wait states before the
 //    MFMA reads it: each asm MFMA starts with s_nop 1, which issues while the
 //    matrix pipe is still busy with the previous MFMA;
-//  * before the results are read back, mfma_acc_done / mfma_vgpr_done wait
+//  * before the results are read back, mfma_acc_done waits
 //    out the MFMA latency (XDL result -> VALU read needs at most 19 wait
 //    states on CDNA3/4), tied to each accumulator so that no read is
 //    scheduled ahead of the wait.
@@ -103,13 +88,6 @@ __device__ __forceinline__ void mfma_acc_done(f32x16_t (&acc)[N]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]));
 #pragma unroll
   for (int i = 1; i < N; ++i) asm volatile("" : "+a"(acc[i]));
-}
-// The same wait for VGPR results of mfma_bagpr before VALU code reads them.
-template <int N>
-__device__ __forceinline__ void mfma_vgpr_done(f32x16_t (&acc)[N]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]));
-#pragma unroll
-  for (int i = 1; i < N; ++i) asm volatile("" : "+v"(acc[i]));
 }
 
 // Pins the computation of x to this point of the instruction stream: the
@@ -207,8 +185,6 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
-
 // Combines x of lane l and lane l ^ 32 with v_permlane32_swap (a VALU op, no
 // LDS round trip).  permlane32_swap(x, x) returns r0 = {x[0..31], x[0..31]}
 // and r1 = {x[32..63], x[32..63]} (checked on the hardware), so every lane
@@ -241,11 +217,6 @@ __device__ __forceinline__ float max32(const f32x16_t& a, const f32x16_t& b) {
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-__device__ __forceinline__ float wave_sum_f(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
