@@ -46,7 +46,7 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
   if (!(p->scale >= 0.0) || !std::isfinite(p->scale)) return BSA_ERR_PARAM_INVALID;
   if ((p->flags & ~(uint32_t)BSA_FLAG_INDEX_BUILT) != 0 || p->reserved != 0) return BSA_ERR_PARAM_INVALID;
   // valid descriptors without a compiled variant
-  if (p->block_x % 64 != 0 || p->block_x > 4096) return BSA_ERR_INNER;
+  if (p->block_x > 4096) return BSA_ERR_INNER;
   if (p->block_y % 64 != 0 || p->block_y > 4096) return BSA_ERR_INNER;
   if (p->kv_layout == BSA_KV_PAGED && p->page_size % 64 != 0) return BSA_ERR_INNER;
   if ((int64_t)p->max_seqlen_kv > (int64_t)p->block_y * 65536 || (int64_t)p->max_seqlen_q > (int64_t)p->block_x * 65536)

@@ -72,6 +72,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   const int my_local = wv * 32 + (lane & 31);
   const int my_row = it.row_lo + my_local;
   const bool row_ok = my_local < it.nrows;
+  // a wave whose 32 rows all lie past the item's rows only helps with the
+  // copies and the barriers
+  const bool wave_active = wv * 32 < it.nrows;
   const int qoff = it.skv - it.sq;
   int kend = it.skv;
   if (CAUSAL) kend = min(kend, it.row_lo + it.nrows - 1 + qoff + 1);
@@ -131,6 +134,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
     more = ld.valid();
     if (more) issue(stage ^ 1, std::false_type{});
+    if (!wave_active) {
+      stage ^= 1;
+      continue;
+    }
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
     const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
@@ -187,18 +194,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 constexpr int QS = 64;  // query rows per staged sub-tile
 
 // Walk over (q-head of the group, q-block of the tile's column list, 64-row
-// part of the q-block: block_x / 64 of them), skipping parts past the
-// sequence end or entirely above the causal limit of the tile's first key.
+// part of the q-block: ceil(block_x / 64) of them, the last one short when
+// block_x is not a multiple of 64), skipping parts past the sequence end or
+// entirely above the causal limit of the tile's first key.
 struct ColWalk {
   const int32_t* col_ptr;
   const int32_t* qrows;
   int hh, e, e1, half;
-  int group, per_head, g, tkb, kg, sq, qoff, key_min, causal, bx, halves;  // halves = bx / QS
+  int group, per_head, g, tkb, kg, sq, qoff, key_min, causal, bx, halves;  // halves = ceil(bx / QS)
   __device__ __forceinline__ int col(int h) const { return (per_head ? g * group + h : g) * tkb + kg; }
   __device__ __forceinline__ bool ok(int qb, int hf) const {
     const int r0 = qb * bx + hf * QS;
     if (r0 >= sq) return false;
-    if (causal && min(r0 + QS, sq) - 1 + qoff < key_min) return false;
+    if (causal && min(min(r0 + QS, (qb + 1) * bx), sq) - 1 + qoff < key_min) return false;
     return true;
   }
   __device__ __forceinline__ void open(int h) {
@@ -227,6 +235,8 @@ struct ColWalk {
     settle();
   }
   __device__ __forceinline__ int row0() const { return ldu(qrows, e) * bx + half * QS; }
+  // end of the current part's rows: the q-block's end or the sequence end
+  __device__ __forceinline__ int row_end() const { return min((ldu(qrows, e) + 1) * bx, sq); }
 };
 
 constexpr int DKDV_WAVES = 2;   // a workgroup's waves, 64 keys each
@@ -319,12 +329,12 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   ld.key_min = key_lo;
   ld.causal = CAUSAL;
   ld.bx = a.seq.bx;
-  ld.halves = a.seq.bx / QS;
+  ld.halves = (a.seq.bx + QS - 1) / QS;
   ld.hh = 0;
   ld.half = 0;
   ld.open(0);
   ld.settle();
-  int r0_next = 0;
+  int r0_next = 0, rend_next = 0;
 
   Dma dma;
   dma.init(qstride);
@@ -335,6 +345,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     const int h = g * a.group + ld.hh;
     const int r0 = ld.row0();
     r0_next = r0;
+    rend_next = ld.row_end();
     const int nvalid = sq - r0;
     const int64_t off = (q0 + r0) * (int64_t)qstride + (int64_t)h * D;
     dma.issue(st, qp + off, nvalid);
@@ -349,8 +360,8 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
   if (more) issue(0);
   int stage = 0;
   while (more) {
-    const int r0 = r0_next;     // the tile computed in this step
-    const int nrows = sq - r0;  // its valid rows (may exceed QS)
+    const int r0 = r0_next;            // the tile computed in this step
+    const int nrows = rend_next - r0;  // its rows inside the q-block and the sequence (may exceed QS)
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // both waves' loads landed; the other stage is no longer read
     more = ld.valid();
@@ -361,8 +372,8 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
     const float* ndll = lsel + QS;
 
-    // Rows past the sequence end, or keys above some row's causal limit,
-    // need masks; every other tile takes the mask-free path.
+    // Rows past the q-block or sequence end, or keys above some row's causal
+    // limit, need masks; every other tile takes the mask-free path.
     const bool masked = nrows < QS || (CAUSAL && key_lo + 127 > r0 + qoff);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile

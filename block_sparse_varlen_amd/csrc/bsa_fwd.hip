@@ -52,10 +52,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   QItem it;
   if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
     return;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int my_local = wv * 32 + (lane & 31);  // row within the item
   const int my_row = it.row_lo + my_local;     // row within the sequence
   const bool row_ok = my_local < it.nrows;
+  // a wave whose 32 rows all lie past the item's rows (short q-blocks, the
+  // sequence end) only helps with the copies and the barriers
+  const bool wave_active = wv * 32 < it.nrows;
   const int qoff = it.skv - it.sq;             // causal: key j allowed for row i when j <= i + qoff
   int kend = it.skv;
   if (CAUSAL) kend = min(kend, it.row_lo + it.nrows - 1 + qoff + 1);
@@ -113,6 +116,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     more = ld.valid();
     if (more) issue(stage ^ 1, std::false_type{});
     settle_scalar_loads();
+    if (!wave_active) {
+      stage ^= 1;
+      continue;
+    }
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + KTILE;
 

@@ -117,7 +117,8 @@ typedef struct bsa_problem {
   int64_t total_kv;          /* T_kv rows of k/v (TND) or number of pages (paged) */
   int32_t max_seqlen_q;      /* upper bound on every Sq_b */
   int32_t max_seqlen_kv;     /* upper bound on every Skv_b */
-  int32_t block_x;           /* q rows per selection block; multiple of 64, <= 4096 */
+  int32_t block_x;           /* q rows per selection block; 1 .. 4096 (work items hold up to 128 rows of one
+                                q-block, so block_x below 128 leaves part of each item idle) */
   int32_t block_y;           /* keys per selection block; multiple of 64 (of 128 for bsa_bwd), <= 4096 */
   int32_t sparse_kind;       /* BSA_SPARSE_* */
   int32_t sparse_heads;      /* Hs: N1 (pattern per q-head) or N2 (shared by a GQA group) */

@@ -81,9 +81,11 @@ def test_workspace_size_ok():
      bsa.BSA_ERR_PARAM_INVALID),  # too few pages per sequence for max_seqlen_kv
     (dict(kv_layout=bsa.BSA_KV_PAGED, page_size=128, max_pages_per_seq=4, page_stride=100),
      bsa.BSA_ERR_PARAM_INVALID),  # page stride shorter than a page
-    (dict(block_x=96), bsa.BSA_ERR_INNER),   # valid, no compiled variant
+    (dict(block_x=96), bsa.BSA_OK),         # work items of 96 rows, a short dK/dV part
+    (dict(block_x=1), bsa.BSA_OK),          # per-token selection
     (dict(block_x=64), bsa.BSA_OK),         # half-height work items
     (dict(block_x=192), bsa.BSA_OK),        # a 128-row and a 64-row work item per q-block
+    (dict(block_x=4097), bsa.BSA_ERR_INNER),  # valid, no compiled variant
     (dict(block_y=48), bsa.BSA_ERR_INNER),
 ])
 def test_stage1_rejects(kw, code):

@@ -59,6 +59,12 @@ def fwd_cases():
                                 kind="mask", bx=192),
         # rows of more than 64 visited blocks (the block list is read 64 entries at a time)
         "none_by64_long_rows": R(115, lens_q=[256, 130], lens_kv=[4500, 9000], N1=2, D=64, kind="none", by=64),
+        # q-blocks shorter than a wave's 32 rows, per-token selection, and
+        # heights that are not multiples of 64
+        "mask_bx16_causal": R(116, lens_q=[150, 77], N1=2, D=128, kind="mask", bx=16, causal=True, density=0.4),
+        "idx_bx1_gqa": R(117, lens_q=[40, 23], lens_kv=[300, 500], N1=4, N2=2, D=64, kind="idx",
+                         sparse_heads=2, bx=1, width=3),
+        "sabi_bx96_f16": R(118, lens_q=[300, 161], N1=2, D=64, dtype="f16", kind="sabi", bx=96),
     }
 
 
@@ -94,6 +100,14 @@ def bwd_cases():
                               paged=True),
         "mask_long_rows_by128": R(214, lens_q=[200, 130], lens_kv=[9000, 12000], N1=2, D=64, kind="mask",
                                   density=0.9),
+        # q-blocks of 16, 1, 96 and 200 rows: dK/dV parts shorter than 64 rows
+        # (the rows past the q-block are masked), per-token selection
+        "mask_bx16_causal": R(215, lens_q=[150, 77], N1=2, D=128, kind="mask", bx=16, causal=True, density=0.4),
+        "idx_bx1_gqa_paged": R(216, lens_q=[40, 23], lens_kv=[300, 500], N1=4, N2=2, D=128, kind="idx",
+                               sparse_heads=2, bx=1, width=3, paged=True),
+        "sabi_bx96_causal_f16": R(217, lens_q=[300, 161], N1=2, D=64, dtype="f16", kind="sabi", bx=96,
+                                  causal=True),
+        "mask_bx200_perhead_gqa": R(218, lens_q=[450, 333], N1=4, N2=2, D=128, kind="mask", bx=200),
     }
 
 
