@@ -9,7 +9,7 @@ resident in HBM.  FLOPs are counted over the selected blocks only: 4 r c D
 per visited (q-head, q-block, kv-block) pair forward and 10 r c D backward
 (r, c = valid rows / columns of the pair).
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+Prints one JSON line.  ``--gpus`` above 1 is refused: the benchmark runs on one
 GPU.
 """
 from __future__ import annotations
@@ -219,7 +219,7 @@ def main():
                     help="also run a 512 MiB elementwise copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
