@@ -200,6 +200,67 @@ def sample_sclk(step, seconds: float = 3.0):
     return (sum(samples) / len(samples), len(samples)) if samples else (None, 0)
 
 
+PEAK_FP8_TFLOPS = 2 * 2516.6  # MI355X dense fp8 MFMA
+
+
+def fp8_main(args, case, workload):
+    """Forward only with FLOAT8_E4M3 q / k / v and bf16 output (the pages'
+    quantType 5): a step is the block index build (no transposed lists) plus
+    one forward call.  Prints one JSON line."""
+    import torch
+    import synth
+    import block_sparse_varlen_amd as bsa
+    from block_sparse_varlen_amd.runner import DeviceCase
+
+    case = synth.to_fp8(case, "bf16")
+    dc = DeviceCase(case, with_bwd=False)
+    idx = dc.index(False)
+    f_fwd = 4.0 * visited_rcd(case, idx)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dc.build_index(False)
+        dc.fwd(prebuilt=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    bsa.bsa_profile_enable(True)
+    bsa.bsa_profile_reset()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for kid, name in bsa.KERNEL_NAMES.items():
+        n, tot = bsa.bsa_profile_read(kid)
+        if n:
+            per_kernel[name] = tot / n
+    bsa.bsa_profile_enable(False)
+    achieved = f_fwd / (per_kernel["fwd"] * 1e-3) / 1e12
+    value = f_fwd / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": "fwd TFLOP/s over selected blocks, e4m3 q/k/v (quantType 5); % of MI355X fp8 MFMA peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (P e4m3, fp32 softmax, bf16 out)",
+        "data": "synthetic (seeded N(0,1) Q/K/V rounded to e4m3, seeded block selection)",
+        "config": {"workload": workload + ", forward only in e4m3"},
+        "frac_of_peak": round(value / PEAK_FP8_TFLOPS, 4),
+        "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "roofline": {"kernel": "fwd", "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     if len(sys.argv) == 4 and sys.argv[1] == "--write-traffic":
         write_traffic(sys.argv[2], sys.argv[3])
@@ -213,6 +274,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5],
                     help="benchmark configuration (default 5, the long-context workload the metric is quoted on)")
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the graphics clock")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward only with e4m3 q/k/v and bf16 output (a separate line; not the default metric)")
     ap.add_argument("--self-index", action="store_true",
                     help="let bsa_fwd and bsa_bwd each build their own block index (no shared build)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -229,8 +292,11 @@ def main():
 
     torch.cuda.set_device(0)
     print("bench: generating inputs", file=sys.stderr, flush=True)
-    case = synth.CONFIGS[args.workload](with_dout=True) if args.workload in (3, 4) else synth.CONFIGS[args.workload]()
     workload = WORKLOAD if args.workload == 5 else OTHER_WORKLOADS[args.workload]
+    if args.fp8:
+        fp8_main(args, synth.CONFIGS[args.workload](), workload)
+        return
+    case = synth.CONFIGS[args.workload](with_dout=True) if args.workload in (3, 4) else synth.CONFIGS[args.workload]()
     dc = DeviceCase(case, with_bwd=True)
     idx = dc.index(False)
     rcd = visited_rcd(case, idx)

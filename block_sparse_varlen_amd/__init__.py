@@ -29,7 +29,7 @@ BSA_ERR_PARAM_INVALID = 161002
 BSA_ERR_INNER = 561103
 BSA_ERR_RUNTIME = 561000
 
-BSA_DTYPE_F16, BSA_DTYPE_BF16 = 1, 2
+BSA_DTYPE_F16, BSA_DTYPE_BF16, BSA_DTYPE_FP8_E4M3 = 1, 2, 3
 BSA_SPARSE_NONE, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_SABI_U16, BSA_SPARSE_IDX_I32 = 0, 1, 2, 3
 BSA_MASK_NONE, BSA_MASK_CAUSAL = 0, 1
 BSA_KV_TND, BSA_KV_PAGED = 0, 1
@@ -68,7 +68,7 @@ class bsa_problem_t(ctypes.Structure):
         ("page_stride", ctypes.c_int64),
         ("scale", ctypes.c_double),
         ("flags", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("out_dtype", ctypes.c_int32),
     ]
 
 

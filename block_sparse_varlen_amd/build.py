@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["bsa_api.cpp", "bsa_index.hip", "bsa_fwd.hip", "bsa_bwd.hip"]
+SOURCES = ["bsa_api.cpp", "bsa_index.hip", "bsa_fwd.hip", "bsa_fwd_fp8.hip", "bsa_bwd.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -24,7 +24,11 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bsa_status_t check_problem(const bsa_problem_t* p) {
   if (!p) return BSA_ERR_PARAM_NULLPTR;
   if (p->struct_size != sizeof(bsa_problem_t)) return BSA_ERR_PARAM_INVALID;
-  if (p->dtype != BSA_DTYPE_F16 && p->dtype != BSA_DTYPE_BF16) return BSA_ERR_PARAM_INVALID;
+  if (p->dtype != BSA_DTYPE_F16 && p->dtype != BSA_DTYPE_BF16 && p->dtype != BSA_DTYPE_FP8_E4M3)
+    return BSA_ERR_PARAM_INVALID;
+  if (p->dtype == BSA_DTYPE_FP8_E4M3 ? (p->out_dtype != BSA_DTYPE_F16 && p->out_dtype != BSA_DTYPE_BF16)
+                                     : (p->out_dtype != 0 && p->out_dtype != p->dtype))
+    return BSA_ERR_PARAM_INVALID;
   if (p->head_dim != 64 && p->head_dim != 128) return BSA_ERR_PARAM_INVALID;
   if (p->batch < 0 || p->total_q < 0 || p->total_kv < 0) return BSA_ERR_PARAM_INVALID;
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return BSA_ERR_PARAM_INVALID;
@@ -44,9 +48,10 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
     if (p->page_stride < (int64_t)p->page_size * row || p->page_stride % row != 0) return BSA_ERR_PARAM_INVALID;
   }
   if (!(p->scale >= 0.0) || !std::isfinite(p->scale)) return BSA_ERR_PARAM_INVALID;
-  if ((p->flags & ~(uint32_t)BSA_FLAG_INDEX_BUILT) != 0 || p->reserved != 0) return BSA_ERR_PARAM_INVALID;
+  if ((p->flags & ~(uint32_t)BSA_FLAG_INDEX_BUILT) != 0) return BSA_ERR_PARAM_INVALID;
   // valid descriptors without a compiled variant
   if (p->block_x > 4096) return BSA_ERR_INNER;
+  if (p->dtype == BSA_DTYPE_FP8_E4M3 && p->head_dim != 128) return BSA_ERR_INNER;
   if (p->block_y % 64 != 0 || p->block_y > 4096) return BSA_ERR_INNER;
   if (p->kv_layout == BSA_KV_PAGED && p->page_size % 64 != 0) return BSA_ERR_INNER;
   if ((int64_t)p->max_seqlen_kv > (int64_t)p->block_y * 65536 || (int64_t)p->max_seqlen_q > (int64_t)p->block_x * 65536)
@@ -56,6 +61,7 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
 
 bsa_status_t check_bwd_variant(const bsa_problem_t* p) {
   if (p->block_y % 128 != 0) return BSA_ERR_INNER;
+  if (p->dtype == BSA_DTYPE_FP8_E4M3) return BSA_ERR_INNER;  // forward-only quantisation
   return BSA_OK;
 }
 
@@ -391,7 +397,9 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
   prof_begin(BSA_KERNEL_FWD, s);
-  e = launch_fwd(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128)), s);
+  const int64_t grid = xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128));
+  e = p->dtype == BSA_DTYPE_FP8_E4M3 ? launch_fwd_fp8(a, p->out_dtype, grid, s)
+                                     : launch_fwd(a, p->dtype, p->head_dim, grid, s);
   prof_end(BSA_KERNEL_FWD, s);
   return from_hip(e);
 }

@@ -157,6 +157,8 @@ struct BwdArgs {
 hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip,
                         int n2, int group, bool with_csc, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t stream);
+// e4m3 q / k / v (head dim 128), out in out_dtype
+hipError_t launch_fwd_fp8(const FwdArgs& a, int out_dtype, int64_t grid, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t stream);

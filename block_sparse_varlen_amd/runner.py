@@ -1,6 +1,6 @@
 """Marshalling helpers: put an input set on the GPU and call the C entry
 points through the binding.  ``case`` is any object with the attributes of
-``synth.Case`` (shapes, dtype, selection and the uint16 ``*_bits`` arrays).
+``synth.Case`` (shapes, dtypes, selection and the ``*_bits`` storage arrays).
 No attention arithmetic happens here.
 """
 from __future__ import annotations
@@ -11,11 +11,13 @@ import numpy as np
 import torch
 
 from . import (
-    BSA_DTYPE_BF16, BSA_DTYPE_F16, BSA_KV_PAGED, BSA_KV_TND, BSA_MASK_CAUSAL, BSA_MASK_NONE,
+    BSA_DTYPE_BF16, BSA_DTYPE_F16, BSA_DTYPE_FP8_E4M3, BSA_KV_PAGED, BSA_KV_TND, BSA_MASK_CAUSAL, BSA_MASK_NONE,
     BSA_FLAG_INDEX_BUILT, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_IDX_I32, BSA_SPARSE_NONE, BSA_SPARSE_SABI_U16,
     bsa_build_index, bsa_bwd, bsa_fwd, bsa_get_workspace_size, bsa_index_view, problem,
 )
 
+_DTYPE = {"bf16": BSA_DTYPE_BF16, "f16": BSA_DTYPE_F16, "fp8": BSA_DTYPE_FP8_E4M3}
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.uint8}
 _KIND = {"none": BSA_SPARSE_NONE, "mask": BSA_SPARSE_BLOCK_MASK, "sabi": BSA_SPARSE_SABI_U16,
          "idx": BSA_SPARSE_IDX_I32}
 
@@ -28,7 +30,8 @@ def problem_for(case):
         lens_kv = np.diff(case.cu_kv)
     sp = case.sparse
     return problem(
-        dtype=BSA_DTYPE_BF16 if case.dtype == "bf16" else BSA_DTYPE_F16,
+        dtype=_DTYPE[case.dtype],
+        out_dtype=_DTYPE[case.out_dtype] if getattr(case, "out_dtype", "") else 0,
         batch=case.B, num_heads_q=case.N1, num_heads_kv=case.N2, head_dim=case.D,
         total_q=int(case.cu_q[-1]), total_kv=int(case.k_bits.shape[0]),
         max_seqlen_q=int(lens_q.max()) if case.B else 0,
@@ -65,8 +68,10 @@ class DeviceCase:
     def __init__(self, case, device="cuda", with_bwd=None):
         self.case = case
         self.p = problem_for(case)
-        tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float16
+        tdt = _TORCH[case.dtype]  # inputs (e4m3 codes as uint8)
+        odt = _TORCH[case.out_dtype] if getattr(case, "out_dtype", "") else tdt  # outputs
         self.tdt = tdt
+        self.odt = odt
         self.q = _dev(case.q_bits, device, tdt)
         self.k = _dev(case.k_bits, device, tdt)
         self.v = _dev(case.v_bits, device, tdt)
@@ -86,7 +91,7 @@ class DeviceCase:
         self.count = _dev(case.count.astype(np.int32), device) if case.count is not None else None
         self.block_table = _dev(case.block_table.astype(np.int32), device) if case.block_table is not None else None
         T, N1, D = int(case.cu_q[-1]), case.N1, case.D
-        self.out = torch.empty((T, N1, D), dtype=tdt, device=device)
+        self.out = torch.empty((T, N1, D), dtype=odt, device=device)
         self.lse = torch.empty((T, N1), dtype=torch.float32, device=device)
         want_bwd = (self.dout is not None) if with_bwd is None else with_bwd
         fwd_b, bwd_b = bsa_get_workspace_size(self.p, True, want_bwd)

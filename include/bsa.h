@@ -69,7 +69,13 @@ typedef enum bsa_status {
   BSA_ERR_RUNTIME = 561000        /* a HIP launch or runtime error */
 } bsa_status_t;
 
-enum { BSA_DTYPE_F16 = 1, BSA_DTYPE_BF16 = 2 };
+/* Element types.  BSA_DTYPE_FP8_E4M3 is FLOAT8_E4M3 (OCP e4m3fn: 4 exponent
+ * bits, bias 7, 3 mantissa bits, no infinities, max 448) for q, k and v of a
+ * forward pass: GenericBlockSparseAttention's quantType 5 (Quantisation
+ * table), where the operator casts P to the same fp8 type itself and no
+ * scale factors are passed; out is fp16 or bf16 (out_dtype).  Head dim 128
+ * only; bsa_bwd has no fp8 variant (BSA_ERR_INNER). */
+enum { BSA_DTYPE_F16 = 1, BSA_DTYPE_BF16 = 2, BSA_DTYPE_FP8_E4M3 = 3 };
 
 /* How the per-q-block KV block selection is given (argument `sparse`). */
 enum {
@@ -108,7 +114,7 @@ enum { BSA_FLAG_INDEX_BUILT = 1u };
 
 typedef struct bsa_problem {
   uint32_t struct_size;      /* sizeof(bsa_problem_t) */
-  int32_t dtype;             /* BSA_DTYPE_*: q, k, v, out, dout, dq, dk, dv */
+  int32_t dtype;             /* BSA_DTYPE_*: q, k, v, dout, and out, dq, dk, dv unless out_dtype says otherwise */
   int32_t batch;             /* B >= 0 */
   int32_t num_heads_q;       /* N1 in [1, 256] */
   int32_t num_heads_kv;      /* N2 >= 1, N1 % N2 == 0, N1 / N2 <= 128 */
@@ -131,7 +137,7 @@ typedef struct bsa_problem {
   int64_t page_stride;       /* paged: elements between pages, >= page_size*N2*D, multiple of N2*D */
   double scale;              /* > 0, or 0 for 1/sqrt(D); applied rounded to fp32 */
   uint32_t flags;            /* BSA_FLAG_* bits, others must be 0 */
-  uint32_t reserved;         /* must be 0 */
+  int32_t out_dtype;         /* 0 (= dtype) or dtype for fp16 / bf16; F16 or BF16 with FP8_E4M3 inputs */
 } bsa_problem_t;
 
 /* Stage 1.  Checks `p` and writes the workspace bytes bsa_fwd (`fwd_bytes`)

@@ -21,8 +21,9 @@ Conventions (shared by every consumer):
   ``[B, max_pages]`` padded with -1 (GenericBlockSparseAttention page,
   "Paged Attention" table).
 
-Tensors are returned twice: ``*_bits`` (uint16 storage pattern, what the GPU
-reads) and the float32 array holding exactly the same rounded values.
+Tensors are returned twice: ``*_bits`` (the storage pattern the GPU reads:
+uint16 for bf16 / fp16, uint8 for fp8) and the float32 array holding exactly
+the same rounded values.
 """
 from __future__ import annotations
 
@@ -34,12 +35,47 @@ import numpy as np
 MASK_NONE, MASK_CAUSAL = 0, 1
 
 
-def round_to_dtype(x: np.ndarray, dtype: str):
-    """Round float32 ``x`` to ``dtype`` ('bf16' or 'f16').
+def _e4m3_table():
+    """Values of the 127 non-negative finite FLOAT8_E4M3 (OCP e4m3fn) codes
+    0x00..0x7E: 4 exponent bits with bias 7, 3 mantissa bits, subnormals at
+    exponent 0, no infinities, 0x7F the NaN."""
+    codes = np.arange(0x7F)
+    e = codes >> 3
+    m = codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7)).astype(np.float64)
 
-    Returns ``(bits uint16, values float32)``.  bf16 uses round-to-nearest-even
-    on the float32 bit pattern; NaN stays NaN.
+
+_E4M3 = _e4m3_table()
+
+
+def round_to_e4m3(x: np.ndarray):
+    """float32 -> FLOAT8_E4M3 (e4m3fn) codes, rounding to nearest with ties to
+    the even code and saturating at +-448; NaN -> 0x7F.  Returns
+    ``(codes uint8, values float32)``."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x.astype(np.float64)), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3, a, side="left"), 0, len(_E4M3) - 1)  # first code >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    pick = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(hi % 2 == 0, hi, lo)))
+    pick = np.where(_E4M3[hi] == a, hi, pick)
+    codes = (pick | np.where(np.signbit(x) & (pick > 0), 0x80, 0)).astype(np.uint8)
+    nan = np.isnan(x)
+    codes[nan] = 0x7F
+    vals = np.where(np.signbit(x) & (pick > 0), -1.0, 1.0) * _E4M3[pick]
+    vals = vals.astype(np.float32)
+    vals[nan] = np.nan
+    return codes, vals
+
+
+def round_to_dtype(x: np.ndarray, dtype: str):
+    """Round float32 ``x`` to ``dtype`` ('bf16', 'f16' or 'fp8' = e4m3fn).
+
+    Returns ``(bits, values float32)``, bits uint16 (uint8 for fp8).  bf16
+    uses round-to-nearest-even on the float32 bit pattern; NaN stays NaN.
     """
+    if dtype == "fp8":
+        return round_to_e4m3(x)
     x = np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "f16":
         h = x.astype(np.float16)
@@ -60,7 +96,8 @@ def round_to_dtype(x: np.ndarray, dtype: str):
 @dataclasses.dataclass
 class Case:
     name: str
-    dtype: str
+    dtype: str  # of q, k, v, dout: 'bf16', 'f16' or 'fp8' (e4m3fn, forward only)
+    out_dtype: str  # of out / dq / dk / dv: '' = dtype; 'bf16' or 'f16' with fp8 inputs
     B: int
     N1: int
     N2: int
@@ -149,7 +186,7 @@ def _values(rng, shape, dtype, nan_mask=None):
     chunks along axis 0 (the generator's stream is the same as one draw).
     ``nan_mask`` (boolean over the leading axes) marks rows set to NaN."""
     shape = tuple(int(x) for x in shape)
-    bits = np.empty(shape, dtype=np.uint16)
+    bits = np.empty(shape, dtype=np.uint8 if dtype == "fp8" else np.uint16)
     vals = np.empty(shape, dtype=np.float32)
     if bits.size == 0:
         return bits, vals
@@ -180,8 +217,20 @@ def _finish(rng, c: dict, with_dout: bool, kv_shape, nan_tail_mask=None, values=
     return Case(**c)
 
 
-def _base(name, dtype, B, N1, N2, D, bx, by, kind, hs, causal, paged, page_size, scale):
-    return dict(name=name, dtype=dtype, B=B, N1=N1, N2=N2, D=D, bx=bx, by=by,
+def to_fp8(case: Case, out_dtype: str = "bf16") -> Case:
+    """The same case with q, k, v re-rounded to FLOAT8_E4M3 (forward only:
+    dout is dropped) and ``out_dtype`` for the output."""
+    c = dataclasses.replace(case, dtype="fp8", out_dtype=out_dtype, name=case.name + "_fp8",
+                            dout_bits=None, dout=None)
+    for n in ("q", "k", "v"):
+        bits, vals = round_to_e4m3(getattr(case, n))
+        setattr(c, n + "_bits", bits)
+        setattr(c, n, vals)
+    return c
+
+
+def _base(name, dtype, B, N1, N2, D, bx, by, kind, hs, causal, paged, page_size, scale, out_dtype=""):
+    return dict(name=name, dtype=dtype, out_dtype=out_dtype, B=B, N1=N1, N2=N2, D=D, bx=bx, by=by,
                 sparse_kind=kind, sparse_heads=hs, causal=causal, paged=paged,
                 page_size=page_size, scale=scale, cu_kv=None, seqused_kv=None,
                 sparse=None, count=None, block_table=None)
@@ -319,7 +368,7 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 def random_case(seed: int, *, lens_q, lens_kv=None, N1=2, N2=None, D=64, dtype="bf16",
                 bx=128, by=128, kind="mask", sparse_heads=None, causal=False, paged=False,
                 page_size=128, density=0.5, width=None, scale=0.0, with_dout=True,
-                messy=False, rows=None, dense_q=False) -> Case:
+                messy=False, rows=None, dense_q=False, out_dtype="") -> Case:
     """Random varlen case.
 
     ``messy`` adds duplicates, unsorted order, out-of-range entries and
@@ -333,7 +382,7 @@ def random_case(seed: int, *, lens_q, lens_kv=None, N1=2, N2=None, D=64, dtype="
     lens_q = [int(x) for x in lens_q]
     lens_kv = list(lens_q) if lens_kv is None else [int(x) for x in lens_kv]
     B = len(lens_q)
-    c = _base(f"rand{seed}", dtype, B, N1, N2, D, bx, by, kind, hs, causal, paged, page_size, scale)
+    c = _base(f"rand{seed}", dtype, B, N1, N2, D, bx, by, kind, hs, causal, paged, page_size, scale, out_dtype)
     c["cu_q"] = _cu(lens_q)
     nqb = [_cdiv(L, bx) for L in lens_q]
     nkb = [_cdiv(L, by) for L in lens_kv]

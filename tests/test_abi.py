@@ -87,6 +87,8 @@ def test_workspace_size_ok():
     (dict(block_x=192), bsa.BSA_OK),        # a 128-row and a 64-row work item per q-block
     (dict(block_x=4097), bsa.BSA_ERR_INNER),  # valid, no compiled variant
     (dict(block_y=48), bsa.BSA_ERR_INNER),
+    (dict(dtype=bsa.BSA_DTYPE_FP8_E4M3), bsa.BSA_ERR_PARAM_INVALID),  # e4m3 needs an fp16 / bf16 out_dtype
+    (dict(dtype=bsa.BSA_DTYPE_BF16, out_dtype=bsa.BSA_DTYPE_F16), bsa.BSA_ERR_PARAM_INVALID),
 ])
 def test_stage1_rejects(kw, code):
     assert status(good(**kw)) == code
@@ -164,3 +166,14 @@ def test_index_view_is_consistent_with_sizes():
     assert v1.max_kv_items == 2 * (600 // 128 + 2)
     # bounds: rows >= every possible Hs * totalQBlocks
     assert v0.max_rows >= 4 * (600 // 128 + 2)
+
+
+def test_fp8_forward_only():
+    """e4m3 inputs: forward with an fp16 / bf16 out_dtype and head dim 128;
+    no backward variant; head dim 64 has no compiled variant."""
+    p = good(dtype=bsa.BSA_DTYPE_FP8_E4M3, out_dtype=bsa.BSA_DTYPE_BF16)
+    assert status(p, fwd=True, bwd=False) == bsa.BSA_OK
+    assert status(p, fwd=False, bwd=True) == bsa.BSA_ERR_INNER
+    assert status(good(dtype=bsa.BSA_DTYPE_FP8_E4M3, out_dtype=bsa.BSA_DTYPE_F16), bwd=False) == bsa.BSA_OK
+    assert status(good(dtype=bsa.BSA_DTYPE_FP8_E4M3, out_dtype=bsa.BSA_DTYPE_F16, head_dim=64),
+                  bwd=False) == bsa.BSA_ERR_INNER
