@@ -53,8 +53,10 @@ __device__ __forceinline__ int pack4_f8(float x0, float x1, float x2, float x3) 
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, r, true);
 }
 
+// Three workgroups per CU (three waves per SIMD: 168 registers each, 32 KiB
+// of LDS per workgroup); two measured 7 % slower.
 template <typename OUT, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(256, 2) void k_fwd_fp8(FwdArgs a) {
+__global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   constexpr int D = 128;         // features (bytes per row)
   using L = XorTile<64>;         // 128-byte rows, 8 XOR-permuted 16-byte chunks
   constexpr int TILE = L::template bytes<KT>();  // 8 KiB
