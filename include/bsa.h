@@ -159,7 +159,7 @@ bsa_status_t bsa_get_workspace_size(const bsa_problem_t* p, size_t* fwd_bytes, s
  *   sparse_count int32 [Hs, sparse_rows] (IDX only, else NULL)
  *   block_table  int32 [B, max_pages_per_seq] (paged only, else NULL); only
  *                entries for pages holding keys < Skv_b are read
- *   out          [T_q, N1, D] dtype
+ *   out          [T_q, N1, D] out_dtype (dtype when out_dtype is 0)
  *   lse          float32 [T_q, N1], natural log of the scaled scores' sum
  * Returns BSA_ERR_PARAM_NULLPTR when a required pointer is NULL,
  * BSA_ERR_PARAM_INVALID when workspace_bytes is below the stage-1 value,
