@@ -29,6 +29,10 @@ def cases():
                               sparse_heads=2, causal=True, paged=True, out_dtype="bf16", **F),
         "none_bx64_long_kv": R(405, lens_q=[100, 180], lens_kv=[1500, 900], N1=2, kind="none", bx=64,
                                out_dtype="bf16", **F),
+        "sabi_bx16_causal_f16": R(406, lens_q=[150, 77], N1=2, kind="sabi", bx=16, causal=True,
+                                  out_dtype="f16", **F),
+        "mask_paged_ps64_perhead": R(407, lens_q=[300, 200], lens_kv=[333, 450], N1=4, N2=2, kind="mask",
+                                     paged=True, page_size=64, out_dtype="bf16", **F),
     }
 
 
