@@ -33,6 +33,8 @@ WORKLOAD = "long-context block-sparse fwd+bwd: TND 2x16384, N1=N2=16, D=128, bf1
 # other workloads for --workload (not the default line): the rest of the
 # benchmark configurations, run fwd + bwd
 OTHER_WORKLOADS = {
+    1: "tiny fwd+bwd: TND, 1 x 512 tokens, N1=N2=2, D=64, fp16, 128x128 blocks, Bernoulli(0.5) block mask "
+       "with the diagonal kept",
     2: "dense varlen causal fwd+bwd: TND, B=4, lengths U{512..4096}, N=16, D=128, bf16, all blocks",
     3: "sabi block-sparse prefill fwd+bwd: B=1, N=32, S=32768, D=128, bf16, block (128,512), keep U{1..16}",
     4: "GQA + paged-KV block-sparse fwd+bwd: B=8, lengths U{1024..8192}, N1=32, N2=8, D=128, bf16, "
@@ -271,7 +273,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="benchmark configuration (default 5, the long-context workload the metric is quoted on)")
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the graphics clock")
     ap.add_argument("--fp8", action="store_true",
@@ -399,7 +401,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"bf16": "bf16", "f16": "fp16"}[case.dtype],
         "data": "synthetic (seeded N(0,1) Q/K/V/dO, seeded block selection)",
         "config": {"workload": workload, "global_batch": case.B, "seq_len": int(np.diff(case.cu_q).max()),
                    "heads": case.N1, "head_dim": case.D, "block_shape": [case.bx, case.by],
