@@ -63,3 +63,32 @@ def test_fwd_fp8(name):
     assert not np.isnan(O).any()
     assert ratio <= 1.0, f"O error above the e4m3 bound ({ratio:.3f})"
     assert lerr <= 1e-3
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n", [3, 5])
+def test_fwd_fp8_config(n):
+    """Full-size sabi prefill and long-context workloads in e4m3 (the
+    bench's --fp8 lines), checked on sampled q-blocks: the longest rows,
+    random ones and every sequence's last q-block."""
+    from test_gpu_parity import _sample_rows
+    print(f"fp8 config {n}: generating", flush=True)
+    case = synth.to_fp8(synth.CONFIGS[n](), "bf16")
+    dc = DeviceCase(case, with_bwd=False)
+    dc.out.fill_(float("nan"))
+    dc.lse.fill_(float("nan"))
+    print(f"fp8 config {n}: fwd on GPU", flush=True)
+    dc.fwd()
+    torch.cuda.synchronize()
+    assert not torch.isnan(dc.out).any() and not torch.isnan(dc.lse).any()
+    idx = oracle.index_products(case, with_csc=False)
+    sample = sorted(_sample_rows(case, idx, 16, n))
+    bound, O_ref = fp8_tol.o_bound(case, sample)
+    _, L_ref = oracle.forward(case, sample)
+    sel = ~np.isnan(L_ref)
+    O = dc.out.float().cpu().numpy()
+    L = dc.lse.cpu().numpy()
+    ratio = float((np.abs(O - O_ref)[sel] / bound[sel]).max())
+    lerr = float(np.abs(L[sel] - L_ref[sel]).max())
+    print(f"  config {n}: rows={int(sel.sum())} max err/bound={ratio:.3f} max|dlse|={lerr:.3e}", flush=True)
+    assert ratio <= 1.0 and lerr <= 1e-3
