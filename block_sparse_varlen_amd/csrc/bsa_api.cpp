@@ -133,7 +133,7 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   L.index_end = off;
   if (with_dl) {
     L.ndl = take((size_t)p->total_q * p->num_heads_q * 4);
-    L.nlse2 = take((size_t)p->total_q * p->num_heads_q * 4);
+    L.lse2 = take((size_t)p->total_q * p->num_heads_q * 4);
   }
   L.total = off;
   return L;
@@ -437,8 +437,8 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   }
 
   float* ndl = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ndl);
-  float* nlse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.nlse2);
-  BwdPreArgs pa{out, dout, lse, ndl, nlse2, p->total_q * p->num_heads_q};
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse2);
+  BwdPreArgs pa{out, dout, lse, ndl, lse2, p->total_q * p->num_heads_q};
   prof_begin(BSA_KERNEL_BWD_PRE, s);
   e = launch_bwd_pre(pa, p->dtype, p->head_dim, s);
   prof_end(BSA_KERNEL_BWD_PRE, s);
@@ -450,7 +450,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.v = v;
   a.dout = dout;
   a.lse = lse;
-  a.nlse2 = nlse2;
+  a.lse2 = lse2;
   a.ndl = ndl;
   a.dq = dq;
   a.dk = dk;

@@ -22,22 +22,10 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Eight packed 16-bit values times c, rounded back to the input type.
-template <typename MF>
-__device__ __forceinline__ u32x4_t scale_op(const u32x4_t& x, float c) {
-  u32x4_t r;
-  r.x = MF::pack(MF::lo(x.x) * c, MF::hi(x.x) * c);
-  r.y = MF::pack(MF::lo(x.y) * c, MF::hi(x.y) * c);
-  r.z = MF::pack(MF::lo(x.z) * c, MF::hi(x.z) * c);
-  r.w = MF::pack(MF::lo(x.w) * c, MF::hi(x.w) * c);
-  return r;
-}
-
 // ------------------------------------------------------------- D = dO.O --
-// One 16-byte chunk per thread, D/8 threads per (token, head) row.  D and
-// lse log2e are stored negated: the dP (and, for bf16, S) accumulators of the
-// dK/dV kernel start from them, so its MFMAs produce dP - D and the exp2
-// argument directly; the dQ kernel's dP^T starts from -D too.
+// One 16-byte chunk per thread, D/8 threads per (token, head) row.  D is
+// stored negated: the dP accumulators of the other two kernels start from
+// -D, so their MFMAs produce dP - D directly.
 template <typename MF, int D>
 __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
   constexpr int CH = D / 8;
@@ -55,7 +43,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
   for (int m = CH / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if (row < a.rows && c == 0) {
     a.ndl[row] = -acc;
-    a.nlse2[row] = -a.lse[row] * LOG2E;
+    a.lse2[row] = a.lse[row] * LOG2E;
   }
 }
 
@@ -202,12 +190,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 //   dV^T += dO^T P,  dK^T += Q^T dS   (Q^T / dO^T via LDS transpose loads,
 //                                      P / dS straight from registers)
 // Every operand read from LDS feeds the MFMAs of both key tiles; dK and dV
-// accumulate in AGPRs.  Without the causal mask and for bf16, the K rows are
-// multiplied by scale log2e once per item (rounded to bf16, whose range is
-// fp32's) and S starts from -lse log2e, so the MFMAs leave the exp2 argument
-// and the softmax needs no per-element multiply-add.  fp16 keeps K as given
-// (a pre-multiplied fp16 K could overflow for scales above ln 2), and so does
-// the causal kernel, whose mask registers leave no room for the -lse tile.
+// accumulate in AGPRs.
 constexpr int QS = 64;  // query rows per staged sub-tile
 
 // Walk over (q-head of the group, q-block of the tile's column list, 64-row
@@ -327,13 +310,6 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
       dv[n][mt] = zero16();
     }
   const float c2 = a.sigma_log2e;
-  constexpr bool PRE = std::is_same<MF, BF16>::value && !CAUSAL;
-  if constexpr (PRE) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kf[n][kk] = scale_op<MF>(kf[n][kk], c2);
-  }
   const int qstride = a.n1 * D;
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* dop = reinterpret_cast<const uint16_t*>(a.dout);
@@ -375,8 +351,8 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     dma.issue(st, qp + off, nvalid);
     dma.issue(st + TILE, dop + off, nvalid);
     float* stat = reinterpret_cast<float*>(st + 2 * TILE);
-    // -lse log2e (wave 0) and -D (wave 1) of the tile's rows
-    dma_rows_f32(stat + wv * QS, (wv == 0 ? a.nlse2 : a.ndl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    // lse (wave 0) and -D (wave 1) of the tile's rows
+    dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.ndl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     ld.next();
   };
 
@@ -393,34 +369,27 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     settle_scalar_loads();
     char* ql = smem + stage * STAGE;
     char* dl_ = ql + TILE;
-    const float* nlsel = reinterpret_cast<const float*>(ql + 2 * TILE);
-    const float* ndll = nlsel + QS;
+    const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
+    const float* ndll = lsel + QS;
 
     // Rows past the q-block or sequence end, or keys above some row's causal
     // limit, need masks; every other tile takes the mask-free path.
     const bool masked = nrows < QS || (CAUSAL && key_lo + 127 > r0 + qoff);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
-      // dP starts from -D of each element's row, so the MFMAs leave dP - D;
-      // S starts from -lse log2e (bf16) or zero
+      // dP starts from -D of each element's row, so the MFMAs leave dP - D
       f32x16_t s[2], dp[2];
       {
-        f32x16_t ndt, nlt;
+        f32x16_t ndt;
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
-          const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
-          const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(ndll + rl);
+          const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(ndll + 32 * h + 8 * ig + 4 * (lane >> 5));
 #pragma unroll
           for (int j = 0; j < 4; ++j) ndt[4 * ig + j] = __uint_as_float(d4[j]);
-          if constexpr (PRE) {
-            const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(nlsel + rl);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) nlt[4 * ig + j] = __uint_as_float(l4[j]);
-          }
         }
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          s[n] = PRE ? nlt : zero16();
+          s[n] = zero16();
           dp[n] = ndt;
         }
       }
@@ -439,14 +408,14 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
       u32x4_t pb[2][2], db[2][2];
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
-        u32x4_t l4 = {};
-        if constexpr (!PRE) l4 = *reinterpret_cast<const u32x4_t*>(nlsel + 32 * h + 8 * ig + 4 * (lane >> 5));
+        const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
+        const u32x4_t l4 = *reinterpret_cast<const u32x4_t*>(lsel + rl);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * ig + j;
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
-            const float p = fast_exp2(PRE ? s[n][i] : fmaf(s[n][i], c2, __uint_as_float(l4[j])));
+            const float p = fast_exp2(fmaf(s[n][i], c2, -__uint_as_float(l4[j])));
             s[n][i] = p;
             dp[n][i] *= p;
           }

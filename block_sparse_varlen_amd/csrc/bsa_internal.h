@@ -45,7 +45,7 @@ struct Layout {
   size_t hdr, sq, skv, qbase, kbase, qb_seq, kb_seq;
   size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work;
   size_t col_cnt, col_ptr, col_fill, qrows, kvkey0, kvval0, kvkey1, kvval1, kvhist, work_kv;
-  size_t ndl, nlse2;
+  size_t ndl, lse2;
   size_t index_end;  // bytes used by the index products
   size_t total;      // bytes needed in all
 };
@@ -117,7 +117,7 @@ struct BwdPreArgs {
   const void* dout;
   const float* lse;
   float* ndl;   // -rowsum(dO o O)
-  float* nlse2;  // -lse * log2(e)
+  float* lse2;  // lse * log2(e)
   int64_t rows; // T_q * N1
 };
 
@@ -127,7 +127,7 @@ struct BwdArgs {
   const void* v;
   const void* dout;
   const float* lse;
-  const float* nlse2;  // -lse * log2(e)
+  const float* lse2;  // lse * log2(e)
   const float* ndl;  // -rowsum(dO o O)
   void* dq;
   void* dk;
