@@ -33,6 +33,9 @@ def cases():
                                   out_dtype="f16", **F),
         "mask_paged_ps64_perhead": R(407, lens_q=[300, 200], lens_kv=[333, 450], N1=4, N2=2, kind="mask",
                                      paged=True, page_size=64, out_dtype="bf16", **F),
+        # a large scale: frequent moves of the reference maximum (P stays <= 256)
+        "mask_scale08": R(408, lens_q=[400, 300], N1=2, kind="mask", scale=0.8, density=0.7, out_dtype="bf16",
+                          **F),
     }
 
 

@@ -3,7 +3,10 @@
 Index products must be bit-exact; floating point must meet the tolerances
 fixed for the method: max-abs error on O <= 1e-2 (bf16) / 5e-3 (fp16), lse
 within 1e-3 (+inf exactly where the oracle has +inf), relative Frobenius error
-on dQ/dK/dV <= 2e-2 (bf16) / 1e-2 (fp16).
+on dQ/dK/dV <= 2e-2 (bf16) / 1e-2 (fp16).  O is stored in the 16-bit input
+type, so its bound also allows half an ulp of that type at the reference
+value (at most 2^-8 |O| for bf16, 2^-11 |O| for fp16): a peaked row whose O is
+one V row of magnitude 4 or more is off by up to 1.6e-2 from storage alone.
 """
 import functools
 import sys
@@ -19,6 +22,7 @@ from block_sparse_varlen_amd.runner import DeviceCase
 pytestmark = pytest.mark.gpu
 
 TOL_O = {"bf16": 1e-2, "f16": 5e-3}
+HALF_ULP = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}  # relative bound on the rounding of O to its type
 TOL_G = {"bf16": 2e-2, "f16": 1e-2}
 TOL_LSE = 1e-3
 
@@ -65,6 +69,11 @@ def fwd_cases():
         "idx_bx1_gqa": R(117, lens_q=[40, 23], lens_kv=[300, 500], N1=4, N2=2, D=64, kind="idx",
                          sparse_heads=2, bx=1, width=3),
         "sabi_bx96_f16": R(118, lens_q=[300, 161], N1=2, D=64, dtype="f16", kind="sabi", bx=96),
+        # large scales: the running maximum often moves by more than the
+        # rescale threshold, so the O^T rescale path runs many times per row
+        "mask_scale08": R(119, lens_q=[600, 333], N1=2, D=128, kind="mask", scale=0.8, density=0.7),
+        "none_causal_scale05_f16": R(120, lens_q=[400, 257], N1=2, D=64, dtype="f16", kind="none", causal=True,
+                                     scale=0.5),
     }
 
 
@@ -136,13 +145,15 @@ def check_fwd(case, dc, sample=None, tag=""):
     sel = ~np.isnan(Lr)
     if sample is None:
         assert sel.all()
-    err = np.abs(O[sel] - Or[sel]).max() if sel.any() else 0.0
+    d = np.abs(O[sel] - Or[sel])
+    err = d.max() if sel.any() else 0.0
+    worst = (d / (TOL_O[case.dtype] + HALF_ULP[case.dtype] * np.abs(Or[sel]))).max() if sel.any() else 0.0
     inf_r = np.isinf(Lr) & sel
     assert np.array_equal(np.isinf(L) & sel, inf_r), f"{tag}: +inf lse positions differ"
     fin = sel & ~inf_r
     lerr = np.abs(L[fin] - Lr[fin]).max() if fin.any() else 0.0
-    say(f"  {tag}: max|dO|={err:.3e} max|dlse|={lerr:.3e} rows={int(sel.sum())}")
-    assert err <= TOL_O[case.dtype], f"{tag}: O error {err}"
+    say(f"  {tag}: max|dO|={err:.3e} (max err/bound {worst:.3f}) max|dlse|={lerr:.3e} rows={int(sel.sum())}")
+    assert worst <= 1.0, f"{tag}: O error {err}"
     assert lerr <= TOL_LSE, f"{tag}: lse error {lerr}"
 
 
