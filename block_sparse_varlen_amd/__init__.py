@@ -4,7 +4,7 @@ MI355X (gfx950).
 Argument marshalling only: every function forwards to the C entry point of the
 same name in ``include/bsa.h``; all computation runs in the HIP library.
 PyTorch supplies device memory and the current HIP stream.  The library must
-have been built (``python -m block_sparse_varlen_amd.build``); importing this
+have been built (``python block_sparse_varlen_amd/build.py``); importing this
 module without it raises ``ImportError``.
 """
 from __future__ import annotations
@@ -97,7 +97,7 @@ class BsaError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_varlen_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python block_sparse_varlen_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, S, VP = ctypes.POINTER, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
     prob = P(bsa_problem_t)

@@ -1,6 +1,7 @@
 """Builds libbsa.so (HIP, gfx950 only) in place, next to this file.
 
-``python -m block_sparse_varlen_amd.build`` or ``build()`` from Python.  Every
+``python block_sparse_varlen_amd/build.py`` or ``build()`` from Python (the package
+itself refuses to import until the library exists).  Every
 call recompiles all sources (objects go to ``_build/`` at the repository root).
 """
 from __future__ import annotations
