@@ -4,10 +4,13 @@ MI355X.
 Workload: the long-context block-sparse case -- 2 sequences x 16384 tokens,
 16 q/kv heads, D = 128, bf16, 128x128 blocks, a block-causal mask keeping the
 diagonal, the 4 preceding and 8 random earlier blocks per q-block.  One step
-= one bsa_fwd + one bsa_bwd call (each rebuilding its block index), inputs
-resident in HBM.  FLOPs are counted over the selected blocks only: 4 r c D
-per visited (q-head, q-block, kv-block) pair forward and 10 r c D backward
-(r, c = valid rows / columns of the pair).
+= one training step's attention: bsa_build_index (with the transposed lists)
+once, then bsa_fwd and bsa_bwd on that index (BSA_FLAG_INDEX_BUILT), inputs
+resident in HBM.  The line also carries each call timed on its own with its
+own index build inside (the unit the per-pass fractions are quoted on).
+FLOPs are counted over the selected blocks only: 4 r c D per visited
+(q-head, q-block, kv-block) pair forward and 10 r c D backward (r, c = valid
+rows / columns of the pair).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: the benchmark runs on one
 GPU.
@@ -81,39 +84,107 @@ def visited_rcd(case, idx):
     return total * hpr * case.D
 
 
-def cpu_baseline(case, budget_s: float):
-    """The CPU oracle (fwd + bwd of whole q-blocks) timed on a random sample of
-    q-blocks of the same workload until ``budget_s`` seconds have passed."""
+def cpu_model() -> str:
+    """The host CPU's model name, read from /proc/cpuinfo (no subprocess)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers() -> int:
+    """Worker processes for the oracle baseline: the CPUs this process may run
+    on, at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+_CPU_CASE = None  # the workload, inherited by the forked oracle workers
+
+
+def _cpu_unit_rcd(case, idx, qbase, b, h, qb):
+    lens_q = np.diff(case.cu_q)
+    rp = idx["row_ptr"]
+    r = h * idx["TQB"] + int(qbase[b]) + qb
+    rows = min(case.bx, int(lens_q[b]) - qb * case.bx)
+    kbs = idx["cols"][rp[r]:rp[r + 1]]
+    c = np.minimum(case.by, int(np.diff(case.cu_kv)[b]) - kbs * case.by).sum()
+    return rows * int(c) * case.D
+
+
+def _cpu_worker(arg):
+    """One oracle worker: whole (sequence, q-head, q-block) units, forward and
+    backward each, drawn at random until the deadline; one BLAS thread."""
+    seed, deadline = arg
     import oracle
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
+    case = _CPU_CASE
     lens_q = np.diff(case.cu_q)
     nqb = -(-lens_q // case.bx)
-    rng = np.random.default_rng(0)
-    idx = oracle.index_products(case, with_csc=False)
-    rp = idx["row_ptr"]
-    TQB = idx["TQB"]
     qbase = np.concatenate([[0], np.cumsum(nqb)])
-    done, flops, t0 = 0, 0.0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+    idx = oracle.index_products(case, with_csc=False)
+    rng = np.random.default_rng(seed)
+    done, flops = 0, 0.0
+    while time.time() < deadline:
         b = int(rng.integers(case.B))
         h = int(rng.integers(case.N1))
         qb = int(rng.integers(nqb[b]))
         oracle.forward(case, sample=[(b, h, qb)])
         oracle.backward(case, sample_rows=[(b, h, qb)])
-        r = h * TQB + int(qbase[b]) + qb
-        rows = min(case.bx, int(lens_q[b]) - qb * case.bx)
-        kbs = idx["cols"][rp[r]:rp[r + 1]]
-        c = np.minimum(case.by, int(np.diff(case.cu_kv)[b]) - kbs * case.by).sum()
-        flops += 14.0 * rows * c * case.D
+        flops += 14.0 * _cpu_unit_rcd(case, idx, qbase, b, h, qb)
         done += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return done, flops
+
+
+def cpu_baseline(case, budget_s: float):
+    """The CPU oracle, as it stands, on random (sequence, q-head, q-block)
+    units of the same workload (forward + backward each), run by a pool of
+    forked worker processes with one BLAS thread each for about ``budget_s``
+    seconds.  Called before the process touches the GPU, so the workers fork
+    from a process without GPU state and nothing is exec'd."""
+    import multiprocessing
+
+    global _CPU_CASE
+    _CPU_CASE = case
+    n = cpu_workers()
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.time()
+    with ctx.Pool(n) as pool:
+        res = pool.map(_cpu_worker, [(1000 + i, t0 + budget_s) for i in range(n)])
+    dt = time.time() - t0
+    _CPU_CASE = None
+    done = sum(r[0] for r in res)
+    flops = sum(r[1] for r in res)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{done} random (sequence, q-head, q-block) units of the same workload, fwd+bwd each, "
-                      f"{dt:.1f} s of fp64 NumPy (BLAS threads={threads})"}
+                      f"{dt:.1f} s of fp64 NumPy over {n} worker processes (1 BLAS thread each)"}
+
+
+def under_profiler() -> bool:
+    """True inside a rocprofv3 run (its environment or preloaded tool
+    library): nothing may be spawned there, as the profiler's preload would
+    follow the child."""
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return True
+    return "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
+def stats_ms(xs):
+    xs = np.sort(np.asarray(xs, dtype=np.float64))
+    return {"median": round(float(np.median(xs)), 4), "min": round(float(xs[0]), 4),
+            "p90": round(float(np.percentile(xs, 90)), 4), "mean": round(float(xs.mean()), 4)}
 
 
 # bench kernel keys by the HIP kernel names rocprofv3 reports
@@ -269,53 +340,65 @@ def main():
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="benchmark configuration (default 5, the long-context workload the metric is quoted on)")
-    ap.add_argument("--no-clock", action="store_true", help="skip sampling the graphics clock")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the graphics clock (always skipped under a profiler)")
     ap.add_argument("--fp8", action="store_true",
                     help="forward only with e4m3 q/k/v and bf16 output (a separate line; not the default metric)")
     ap.add_argument("--self-index", action="store_true",
-                    help="let bsa_fwd and bsa_bwd each build their own block index (no shared build)")
+                    help="the step lets bsa_fwd and bsa_bwd each build their own block index (no shared build)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 512 MiB elementwise copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    profiled = under_profiler()
+    if profiled:
+        args.no_clock = True
+        args.no_cpu_baseline = True
 
     import torch
     import synth
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    workload = WORKLOAD if args.workload == 5 else OTHER_WORKLOADS[args.workload]
+    if args.fp8:
+        import block_sparse_varlen_amd  # noqa: F401  (fails loudly without the library)
+        torch.cuda.set_device(0)
+        fp8_main(args, synth.CONFIGS[args.workload](), workload)
+        return
+    case = synth.CONFIGS[args.workload](with_dout=True) if args.workload in (3, 4) else synth.CONFIGS[args.workload]()
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is touched: the oracle workers fork from this process
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, args.cpu_budget)
+
     import block_sparse_varlen_amd as bsa
     from block_sparse_varlen_amd.runner import DeviceCase
 
     torch.cuda.set_device(0)
-    print("bench: generating inputs", file=sys.stderr, flush=True)
-    workload = WORKLOAD if args.workload == 5 else OTHER_WORKLOADS[args.workload]
-    if args.fp8:
-        fp8_main(args, synth.CONFIGS[args.workload](), workload)
-        return
-    case = synth.CONFIGS[args.workload](with_dout=True) if args.workload in (3, 4) else synth.CONFIGS[args.workload]()
     dc = DeviceCase(case, with_bwd=True)
     idx = dc.index(False)
     rcd = visited_rcd(case, idx)
     f_fwd, f_bwd = 4.0 * rcd, 10.0 * rcd
     stream = torch.cuda.current_stream()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     # one training step: the block index is built once (bsa_build_index, with
     # the transposed lists) and both passes run on it (BSA_FLAG_INDEX_BUILT)
     shared = not args.self_index
 
-    def fwd_part():
+    def step():
         if shared:
             dc.build_index(True)
         dc.fwd(prebuilt=shared)
-
-    def step():
-        fwd_part()
         dc.bwd(prebuilt=shared)
 
     print("bench: warmup", file=sys.stderr, flush=True)
@@ -323,33 +406,51 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # whole-step timing (HIP events on the launch stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # whole-step timing (HIP events on the launch stream): the K steps as one
+    # bracket, and each step's own bracket for the median / min / p90
+    print("bench: timed steps", file=sys.stderr, flush=True)
+    ev = [(E(), E()) for _ in range(args.steps)]
+    e0, e1 = E(), E()
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        ev[k][0].record(stream)
         step()
+        ev[k][1].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    step_stats = stats_ms([a.elapsed_time(b) for a, b in ev])
 
-    # split: index build, forward call, backward call -- events between the
-    # calls of back-to-back steps, one synchronisation at the end, so no
-    # bracket starts on an idle GPU waiting for its first launch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # split of the shared-index step: index build, forward call, backward call
+    # -- events between the calls of back-to-back steps, one synchronisation
+    # at the end, so no bracket starts on an idle GPU
+    ev = [[E() for _ in range(4)] for _ in range(args.steps)]
     for k in range(args.steps):
         ev[k][0].record(stream)
-        if shared:
-            dc.build_index(True)
+        dc.build_index(True)
         ev[k][1].record(stream)
-        dc.fwd(prebuilt=shared)
+        dc.fwd(prebuilt=True)
         ev[k][2].record(stream)
-        dc.bwd(prebuilt=shared)
+        dc.bwd(prebuilt=True)
         ev[k][3].record(stream)
     torch.cuda.synchronize()
-    idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    idx_st = stats_ms([e[0].elapsed_time(e[1]) for e in ev])
+    fwd_st = stats_ms([e[1].elapsed_time(e[2]) for e in ev])
+    bwd_st = stats_ms([e[2].elapsed_time(e[3]) for e in ev])
+
+    # each call on its own, building its own index inside (the unit the
+    # per-pass fractions are quoted on)
+    ev = [[E() for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        dc.fwd()
+        ev[k][1].record(stream)
+        dc.bwd()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    fwd_call = stats_ms([e[0].elapsed_time(e[1]) for e in ev])
+    bwd_call = stats_ms([e[1].elapsed_time(e[2]) for e in ev])
 
     # per-kernel durations from events the library records around its launches
     bsa.bsa_profile_enable(True)
@@ -389,6 +490,10 @@ def main():
         if ent and ent.get("source_sha") == kernel_source_sha(dominant):
             traffic = ent.get("bytes_per_launch")
 
+    def rate(flops, ms):
+        t = flops / (ms * 1e-3) / 1e12
+        return {"tflops": round(t, 3), "frac_of_peak": round(t / PEAK_BF16_TFLOPS, 4)}
+
     total_tflops = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -407,13 +512,15 @@ def main():
                    "heads": case.N1, "head_dim": case.D, "block_shape": [case.bx, case.by],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
-        # the block index (built once per step and used by both passes; inside
-        # each call with --self-index) and the two attention calls
-        "index": {"ms": round(idx_ms, 4), "shared": shared},
-        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
-                "frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": f_fwd},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
-                "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": f_bwd},
+        "step_ms": step_stats,
+        # each call on its own, its own index build inside (median over the
+        # timed iterations): the per-pass rates
+        "fwd_call": dict(ms=fwd_call, flops=f_fwd, **rate(f_fwd, fwd_call["median"])),
+        "bwd_call": dict(ms=bwd_call, flops=f_bwd, **rate(f_bwd, bwd_call["median"])),
+        # the shared-index step split into its three brackets (medians)
+        "index": {"ms": idx_st},
+        "fwd": dict(ms=fwd_st, **rate(f_fwd, fwd_st["median"])),
+        "bwd": dict(ms=bwd_st, **rate(f_bwd, bwd_st["median"])),
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per_kernel.items()},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -423,12 +530,8 @@ def main():
         "clock": {"sclk_mhz": round(sclk, 1) if sclk else None, "samples": nsamp,
                   "method": "amd-smi metric --clock, mean over XCDs, while steps run back to back",
                   "frac_of_peak_at_sclk": round(total_tflops / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4) if sclk else None},
+        "cpu_baseline": cpu,
     }
-    if not args.no_cpu_baseline:
-        print("bench: cpu baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
-    else:
-        line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
 
 

@@ -50,3 +50,29 @@ def test_traffic_scaling(tmp_path, monkeypatch):
     assert t["fwd"]["source_sha"] == bench.kernel_source_sha("fwd")
     assert t["bwd_pre"]["bytes_per_launch"] == 50 * 1024 * 2 + 8 * 1024
     assert "source_sha" not in t["bwd_pre"]
+
+
+def test_profiler_detection(monkeypatch):
+    """Under rocprofv3 (its ROCPROF* environment or its preloaded tool
+    library) the bench spawns nothing: no clock sampling, no oracle pool."""
+    for k in list(os.environ):
+        if k.startswith("ROCPROF"):
+            monkeypatch.delenv(k)
+    monkeypatch.setenv("LD_PRELOAD", "")
+    assert not bench.under_profiler()
+    monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp/x")
+    assert bench.under_profiler()
+    monkeypatch.delenv("ROCPROF_OUTPUT_PATH")
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
+    assert bench.under_profiler()
+
+
+def test_step_statistics():
+    st = bench.stats_ms([3.0, 1.0, 2.0, 10.0, 4.0])
+    assert st["median"] == 3.0 and st["min"] == 1.0 and st["mean"] == 4.0
+    assert 4.0 < st["p90"] <= 10.0
+
+
+def test_cpu_workers_bounded():
+    assert 1 <= bench.cpu_workers() <= 16
+    assert isinstance(bench.cpu_model(), str)

@@ -4,9 +4,12 @@ Index products must be bit-exact; floating point must meet the tolerances
 fixed for the method: max-abs error on O <= 1e-2 (bf16) / 5e-3 (fp16), lse
 within 1e-3 (+inf exactly where the oracle has +inf), relative Frobenius error
 on dQ/dK/dV <= 2e-2 (bf16) / 1e-2 (fp16).  O is stored in the 16-bit input
-type, so its bound also allows half an ulp of that type at the reference
-value (at most 2^-8 |O| for bf16, 2^-11 |O| for fp16): a peaked row whose O is
-one V row of magnitude 4 or more is off by up to 1.6e-2 from storage alone.
+type: where half an ulp of that type at the reference value (at most
+2^-8 |O| for bf16, 2^-11 |O| for fp16) exceeds the bound by itself -- a peaked
+row whose O is nearly one V row of magnitude above 2.56 (bf16) -- the bound
+for that element is the tolerance plus that half-ulp; every other element is
+held to the literal tolerance.  Each check prints how many elements exceed the
+literal tolerance and by how much.
 """
 import functools
 import sys
@@ -33,6 +36,14 @@ def say(msg):
 
 
 # ------------------------------------------------------------------- cases --
+
+def _short_idx(case, rows):
+    """The case with its idx / count tensors cut to their first `rows` global
+    q-blocks (fewer than totalQBlocks)."""
+    case.sparse = np.ascontiguousarray(case.sparse[:, :rows])
+    case.count = np.ascontiguousarray(case.count[:, :rows])
+    return case
+
 
 def fwd_cases():
     R = synth.random_case
@@ -74,6 +85,19 @@ def fwd_cases():
         "mask_scale08": R(119, lens_q=[600, 333], N1=2, D=128, kind="mask", scale=0.8, density=0.7),
         "none_causal_scale05_f16": R(120, lens_q=[400, 257], N1=2, D=64, dtype="f16", kind="none", causal=True,
                                      scale=0.5),
+        # a sequence with queries but no keys (O = 0, lse = +inf for all its rows)
+        "mask_skv0_seq": R(121, lens_q=[300, 200, 150], lens_kv=[400, 0, 260], N1=2, D=64, kind="mask"),
+        "idx_skv0_paged_causal": R(122, lens_q=[260, 130], lens_kv=[0, 300], N1=4, N2=2, D=128, kind="idx",
+                                   sparse_heads=2, causal=True, paged=True, messy=True),
+        # selection tensors with fewer rows than q-blocks: the rows past them select nothing
+        "mask_short_rows": R(123, lens_q=[700, 300], N1=2, D=64, kind="mask", rows=2, density=0.8),
+        "sabi_short_rows_causal": R(124, lens_q=[520, 640], N1=2, D=128, kind="sabi", rows=3, causal=True),
+        "idx_short_rows": _short_idx(R(125, lens_q=[600, 400], N1=4, N2=2, D=64, kind="idx", sparse_heads=2), 5),
+        # the largest BlitzSparseAttention block shapes: 1024-row q-blocks
+        # (8 work items each) and 1024-key KV blocks
+        "mask_bx1024_by1024": R(126, lens_q=[2500, 1100], N1=2, D=64, kind="mask", bx=1024, by=1024, density=0.7),
+        "sabi_bx1024_by1024_causal": R(127, lens_q=[2100, 1500], N1=2, D=128, kind="sabi", bx=1024, by=1024,
+                                       causal=True),
     }
 
 
@@ -122,6 +146,18 @@ def bwd_cases():
         # in dK and dV
         "mask_d64_scale08": R(219, lens_q=[300, 257], N1=2, D=64, kind="mask", scale=0.8),
         "none_scale08_f16": R(220, lens_q=[200, 140], N1=2, D=128, dtype="f16", kind="none", scale=0.8),
+        # a sequence with queries but no keys: its dQ is 0
+        "mask_skv0_seq": R(221, lens_q=[300, 200, 150], lens_kv=[400, 0, 260], N1=2, D=64, kind="mask"),
+        "idx_skv0_paged_causal": R(222, lens_q=[260, 130], lens_kv=[0, 300], N1=4, N2=2, D=128, kind="idx",
+                                   sparse_heads=2, causal=True, paged=True, messy=True),
+        # selection tensors with fewer rows than q-blocks
+        "mask_short_rows": R(223, lens_q=[700, 300], N1=2, D=64, kind="mask", rows=2, density=0.8),
+        "idx_short_rows_perhead": _short_idx(R(224, lens_q=[600, 400], N1=4, N2=2, D=64, kind="idx",
+                                               sparse_heads=4), 4),
+        # 1024 x 1024 blocks
+        "mask_bx1024_by1024": R(225, lens_q=[2500, 1100], N1=2, D=64, kind="mask", bx=1024, by=1024, density=0.7),
+        "sabi_bx1024_by1024_causal_f16": R(226, lens_q=[2100, 1500], N1=2, D=128, dtype="f16", kind="sabi",
+                                           bx=1024, by=1024, causal=True),
     }
 
 
@@ -147,12 +183,19 @@ def check_fwd(case, dc, sample=None, tag=""):
         assert sel.all()
     d = np.abs(O[sel] - Or[sel])
     err = d.max() if sel.any() else 0.0
-    worst = (d / (TOL_O[case.dtype] + HALF_ULP[case.dtype] * np.abs(Or[sel]))).max() if sel.any() else 0.0
+    tol = TOL_O[case.dtype]
+    store = HALF_ULP[case.dtype] * np.abs(Or[sel])  # bound on rounding O to its type
+    bound = np.where(store > tol, tol + store, tol)
+    worst = (d / bound).max() if sel.any() else 0.0
+    over = d > tol
+    n_over = int(over.sum())
+    lit = f"literal {tol:g}: {n_over} over" + (f" (max {d[over].max():.3e} at |O|={np.abs(Or[sel])[over].max():.2f})"
+                                             if n_over else "")
     inf_r = np.isinf(Lr) & sel
     assert np.array_equal(np.isinf(L) & sel, inf_r), f"{tag}: +inf lse positions differ"
     fin = sel & ~inf_r
     lerr = np.abs(L[fin] - Lr[fin]).max() if fin.any() else 0.0
-    say(f"  {tag}: max|dO|={err:.3e} (max err/bound {worst:.3f}) max|dlse|={lerr:.3e} rows={int(sel.sum())}")
+    say(f"  {tag}: max|dO|={err:.3e} (max err/bound {worst:.3f}; {lit}) max|dlse|={lerr:.3e} rows={int(sel.sum())}")
     assert worst <= 1.0, f"{tag}: O error {err}"
     assert lerr <= TOL_LSE, f"{tag}: lse error {lerr}"
 
