@@ -4,12 +4,12 @@ Index products must be bit-exact; floating point must meet the tolerances
 fixed for the method: max-abs error on O <= 1e-2 (bf16) / 5e-3 (fp16), lse
 within 1e-3 (+inf exactly where the oracle has +inf), relative Frobenius error
 on dQ/dK/dV <= 2e-2 (bf16) / 1e-2 (fp16).  O is stored in the 16-bit input
-type: where half an ulp of that type at the reference value (at most
-2^-8 |O| for bf16, 2^-11 |O| for fp16) exceeds the bound by itself -- a peaked
-row whose O is nearly one V row of magnitude above 2.56 (bf16) -- the bound
-for that element is the tolerance plus that half-ulp; every other element is
-held to the literal tolerance.  Each check prints how many elements exceed the
-literal tolerance and by how much.
+type, so an element may also be off by the rounding to that type: the bound of
+an element is the tolerance plus the exact half-ulp of the output type at
+|O_ref| + tolerance (2^(e-8) for bf16, 2^(e-11) for fp16, e the binary
+exponent).  A peaked row whose O is nearly one V row of magnitude 2..4 loses
+up to 7.8e-3 (bf16) to storage alone.  Each check prints how many elements
+exceed the literal tolerance and by how much.
 """
 import functools
 import sys
@@ -25,7 +25,7 @@ from block_sparse_varlen_amd.runner import DeviceCase
 pytestmark = pytest.mark.gpu
 
 TOL_O = {"bf16": 1e-2, "f16": 5e-3}
-HALF_ULP = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}  # relative bound on the rounding of O to its type
+SIG_BITS = {"bf16": 8, "f16": 11}  # significand bits of the output type
 TOL_G = {"bf16": 2e-2, "f16": 1e-2}
 TOL_LSE = 1e-3
 
@@ -174,6 +174,13 @@ def empty_rows_case():
 
 # ----------------------------------------------------------------- helpers --
 
+def half_ulp(x, dtype):
+    """Half an ulp of the 16-bit type at magnitude x (normal range): the most
+    that rounding a value of that size to the type can move it."""
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -14)))
+    return 2.0 ** (e - SIG_BITS[dtype])
+
+
 def check_fwd(case, dc, sample=None, tag=""):
     O = dc.out.float().cpu().numpy()
     L = dc.lse.cpu().numpy()
@@ -184,8 +191,7 @@ def check_fwd(case, dc, sample=None, tag=""):
     d = np.abs(O[sel] - Or[sel])
     err = d.max() if sel.any() else 0.0
     tol = TOL_O[case.dtype]
-    store = HALF_ULP[case.dtype] * np.abs(Or[sel])  # bound on rounding O to its type
-    bound = np.where(store > tol, tol + store, tol)
+    bound = tol + half_ulp(np.abs(Or[sel]) + tol, case.dtype)
     worst = (d / bound).max() if sel.any() else 0.0
     over = d > tol
     n_over = int(over.sum())
