@@ -38,7 +38,7 @@ BSA_FLAG_INDEX_BUILT = 1
 KERNEL_NAMES = {0: "index", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq"}
 
 EXPORTS = (
-    "bsa_get_workspace_size", "bsa_fwd", "bsa_bwd", "bsa_index_view", "bsa_build_index",
+    "bsa_get_workspace_size", "bsa_fwd", "bsa_fwd_noalloc", "bsa_bwd", "bsa_index_view", "bsa_build_index",
     "bsa_status_string", "bsa_profile_enable", "bsa_profile_reset", "bsa_profile_read",
 )
 
@@ -103,6 +103,7 @@ def _load():
     prob = P(bsa_problem_t)
     lib.bsa_get_workspace_size.argtypes = [prob, P(S), P(S)]
     lib.bsa_fwd.argtypes = [prob] + [VP] * 11 + [VP, S, VP]
+    lib.bsa_fwd_noalloc.argtypes = [prob] + [VP] * 11 + [VP]
     lib.bsa_bwd.argtypes = [prob] + [VP] * 15 + [VP, S, VP]
     lib.bsa_index_view.argtypes = [prob, I, P(bsa_index_view_t)]
     lib.bsa_build_index.argtypes = [prob, VP, VP, VP, VP, VP, I, VP, S, VP]
@@ -168,6 +169,17 @@ def bsa_fwd(p, q, k, v, cu_seqlens_q, cu_seqlens_kv, seqused_kv, sparse, sparse_
                       _ptr(seqused_kv), _ptr(sparse), _ptr(sparse_count), _ptr(block_table), _ptr(out), _ptr(lse),
                       _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check(st, "bsa_fwd")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # BSA_NOALLOC_SCRATCH_BYTES
+
+
+def bsa_fwd_noalloc(p, q, k, v, cu_seqlens_q, cu_seqlens_kv, seqused_kv, sparse, sparse_count, block_table,
+                    out, lse, stream=None):
+    st = _lib.bsa_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                              _ptr(cu_seqlens_kv), _ptr(seqused_kv), _ptr(sparse), _ptr(sparse_count),
+                              _ptr(block_table), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "bsa_fwd_noalloc")
 
 
 def bsa_bwd(p, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, seqused_kv, sparse, sparse_count,

@@ -13,6 +13,39 @@
 
 using namespace bsa;
 
+// Device scratch of bsa_fwd_noalloc: it stands in for the workspace argument
+// (the block index) of callers that cannot allocate device memory.  Each GPU
+// the library runs on holds its own copy for the life of the process.  In host
+// code `scratch` is only a host-side handle of the symbol, never a device
+// address: its address on a device comes from hipGetSymbolAddress (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[BSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+bsa_status_t scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BSA_ERR_RUNTIME;
+  if (dev >= kMaxDevices) return BSA_ERR_INNER;
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s]() { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess || !s.ptr) return BSA_ERR_RUNTIME;
+  *out = s.ptr;
+  return BSA_OK;
+}
+
+}  // namespace
+
 namespace {
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -250,6 +283,67 @@ void prof_drain(ProfState& s) {
   s.recs.clear();
 }
 
+bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, const void* v, const int64_t* cu_q,
+                     const int64_t* cu_kv, const int32_t* seqused, const void* sparse, const int32_t* count,
+                     const int32_t* block_table, void* out, float* lse, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  bsa_status_t st = check_problem(p);
+  if (st != BSA_OK) return st;
+  const Bounds b = make_bounds(p);
+  if (!bounds_fit(b)) return BSA_ERR_PARAM_INVALID;
+  const Layout L = make_layout(p, b, false, false);
+  if (p->batch == 0 || p->total_q == 0) return BSA_OK;
+  if (!q || !out || !lse) return BSA_ERR_PARAM_NULLPTR;
+  if (p->total_kv > 0 && (!k || !v)) return BSA_ERR_PARAM_NULLPTR;
+  st = check_index_ptrs(p, cu_q, cu_kv, seqused, sparse, count);
+  if (st != BSA_OK) return st;
+  if (p->kv_layout == BSA_KV_PAGED && !block_table) return BSA_ERR_PARAM_NULLPTR;
+  if (!workspace) return BSA_ERR_PARAM_NULLPTR;
+  if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const IndexPtrs ip = make_ptrs(workspace, L, false);
+  const int group = p->num_heads_q / p->num_heads_kv;
+  const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
+  hipError_t e = hipSuccess;
+  if (!(p->flags & BSA_FLAG_INDEX_BUILT)) {
+    prof_begin(BSA_KERNEL_INDEX, s);
+    e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, false, s);
+    prof_end(BSA_KERNEL_INDEX, s);
+    if (e != hipSuccess) return BSA_ERR_RUNTIME;
+  }
+
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.seq = seq;
+  a.block_table = block_table;
+  a.hdr = ip.hdr;
+  a.qb_seq = ip.qb_seq;
+  a.qbase = ip.qbase;
+  a.row_ptr = ip.row_ptr;
+  a.cols = ip.cols;
+  a.work = ip.work;
+  a.n1 = p->num_heads_q;
+  a.n2 = p->num_heads_kv;
+  a.group = group;
+  a.heads_per_row = p->sparse_heads == p->num_heads_q ? 1 : group;
+  a.page_size = p->kv_layout == BSA_KV_PAGED ? p->page_size : 0;
+  a.max_pages = p->kv_layout == BSA_KV_PAGED ? p->max_pages_per_seq : 0;
+  a.page_stride = p->kv_layout == BSA_KV_PAGED ? p->page_stride : 0;
+  a.sigma = sigma_of(p);
+  a.sigma_log2e = a.sigma * 1.4426950408889634f;
+  prof_begin(BSA_KERNEL_FWD, s);
+  const int64_t grid = xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128));
+  e = p->dtype == BSA_DTYPE_FP8_E4M3 ? launch_fwd_fp8(a, p->out_dtype, grid, s)
+                                     : launch_fwd(a, p->dtype, p->head_dim, grid, s);
+  prof_end(BSA_KERNEL_FWD, s);
+  return from_hip(e);
+}
+
 }  // namespace
 
 namespace bsa {
@@ -347,61 +441,29 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
                      const int64_t* cu_kv, const int32_t* seqused, const void* sparse, const int32_t* count,
                      const int32_t* block_table, void* out, float* lse, void* workspace, size_t ws_bytes,
                      void* stream) {
+  return fwd_impl(p, q, k, v, cu_q, cu_kv, seqused, sparse, count, block_table, out, lse, workspace, ws_bytes,
+                  stream);
+}
+
+bsa_status_t bsa_fwd_noalloc(const bsa_problem_t* p, const void* q, const void* k, const void* v,
+                             const int64_t* cu_q, const int64_t* cu_kv, const int32_t* seqused, const void* sparse,
+                             const int32_t* count, const int32_t* block_table, void* out, float* lse,
+                             void* stream) {
   bsa_status_t st = check_problem(p);
   if (st != BSA_OK) return st;
+  // the index of this entry point lives in the library's scratch array, so a
+  // prebuilt one cannot be handed in
+  if (p->flags & BSA_FLAG_INDEX_BUILT) return BSA_ERR_PARAM_INVALID;
   const Bounds b = make_bounds(p);
   if (!bounds_fit(b)) return BSA_ERR_PARAM_INVALID;
-  const Layout L = make_layout(p, b, false, false);
+  const size_t need = make_layout(p, b, false, false).total;
+  if (need > (size_t)BSA_NOALLOC_SCRATCH_BYTES) return BSA_ERR_PARAM_INVALID;
   if (p->batch == 0 || p->total_q == 0) return BSA_OK;
-  if (!q || !out || !lse) return BSA_ERR_PARAM_NULLPTR;
-  if (p->total_kv > 0 && (!k || !v)) return BSA_ERR_PARAM_NULLPTR;
-  st = check_index_ptrs(p, cu_q, cu_kv, seqused, sparse, count);
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
   if (st != BSA_OK) return st;
-  if (p->kv_layout == BSA_KV_PAGED && !block_table) return BSA_ERR_PARAM_NULLPTR;
-  if (!workspace) return BSA_ERR_PARAM_NULLPTR;
-  if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const IndexPtrs ip = make_ptrs(workspace, L, false);
-  const int group = p->num_heads_q / p->num_heads_kv;
-  const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
-  hipError_t e = hipSuccess;
-  if (!(p->flags & BSA_FLAG_INDEX_BUILT)) {
-    prof_begin(BSA_KERNEL_INDEX, s);
-    e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, false, s);
-    prof_end(BSA_KERNEL_INDEX, s);
-    if (e != hipSuccess) return BSA_ERR_RUNTIME;
-  }
-
-  FwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.lse = lse;
-  a.seq = seq;
-  a.block_table = block_table;
-  a.hdr = ip.hdr;
-  a.qb_seq = ip.qb_seq;
-  a.qbase = ip.qbase;
-  a.row_ptr = ip.row_ptr;
-  a.cols = ip.cols;
-  a.work = ip.work;
-  a.n1 = p->num_heads_q;
-  a.n2 = p->num_heads_kv;
-  a.group = group;
-  a.heads_per_row = p->sparse_heads == p->num_heads_q ? 1 : group;
-  a.page_size = p->kv_layout == BSA_KV_PAGED ? p->page_size : 0;
-  a.max_pages = p->kv_layout == BSA_KV_PAGED ? p->max_pages_per_seq : 0;
-  a.page_stride = p->kv_layout == BSA_KV_PAGED ? p->page_stride : 0;
-  a.sigma = sigma_of(p);
-  a.sigma_log2e = a.sigma * 1.4426950408889634f;
-  prof_begin(BSA_KERNEL_FWD, s);
-  const int64_t grid = xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128));
-  e = p->dtype == BSA_DTYPE_FP8_E4M3 ? launch_fwd_fp8(a, p->out_dtype, grid, s)
-                                     : launch_fwd(a, p->dtype, p->head_dim, grid, s);
-  prof_end(BSA_KERNEL_FWD, s);
-  return from_hip(e);
+  return fwd_impl(p, q, k, v, cu_q, cu_kv, seqused, sparse, count, block_table, out, lse, ws,
+                  (size_t)BSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const void* v, const void* out,

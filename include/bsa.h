@@ -170,6 +170,25 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
                      const int32_t* block_table, void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments and results as bsa_fwd without the workspace:
+ * the block index is built in a device array the library owns, one per GPU
+ * (BSA_NOALLOC_SCRATCH_BYTES, held until the process ends; its device address
+ * is looked up once per device on the first call there, with that device
+ * current).  Every call on a GPU shares that GPU's array and overwrites it:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give undefined results; calls ordered on one stream are safe.  Returns
+ * BSA_ERR_PARAM_INVALID when the problem's forward workspace
+ * (bsa_get_workspace_size's fwd_bytes) exceeds the array or when
+ * BSA_FLAG_INDEX_BUILT is set, before any device work.  Allocates nothing
+ * (no hipMalloc / hipFree / allocating library call). */
+#define BSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+bsa_status_t bsa_fwd_noalloc(const bsa_problem_t* p, const void* q, const void* k, const void* v,
+                             const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                             const int32_t* seqused_kv, const void* sparse, const int32_t* sparse_count,
+                             const int32_t* block_table, void* out, float* lse, void* stream);
+
 /* Stage 2, backward.  Inputs as bsa_fwd plus `out` and `lse` from the forward
  * pass and `dout` [T_q, N1, D].  Outputs dq [T_q, N1, D], dk and dv with k's
  * shape.  In the paged layout dk / dv are written at the (page, slot) of every
