@@ -25,11 +25,23 @@ approximation), with the passage each part follows:
 * Causal masking aligned at the bottom-right corner (FlashAttention
   UnpaddingScoreGradV2 page, sparseMode table, rightDownCausal, the only
   causal form its TND layout accepts).
+* Band masking (sparseMode 4, "band", on the FlashAttention
+  UnpaddingScoreGradV2 page, section 6.6, and the BlitzSparseAttention page's
+  sparseMode limits): query ``i`` may attend to keys ``j`` with
+  ``i + Skv - Sq - preTokens <= j <= i + Skv - Sq + nextTokens``, where
+  preTokens counts the earlier tokens the sliding window keeps and nextTokens
+  the later ones (PromptFlashAttention page, attribute table; the
+  BlockSparseAttentionGrad README's preTokens / nextTokens rows).  The
+  alignment at the bottom-right corner is the reading that the
+  BlitzSparseAttention page's row-dropping conditions for band support (rows
+  fall out when preTokens < 0, or when nextTokens + Skv - Sq < 0); the causal
+  mask is the band with an unbounded preTokens and nextTokens = 0.
 
 Readings where the pages are silent (each listed in the design doc): a selection is
 a *set* (duplicates count once, order is irrelevant); entries outside
 ``[0, nKB_b)`` are skipped; counts are clamped to ``[0, W]``; KV indices are
-local to the sequence; ``g(h) = h // (N1 / N2)``; a query row with no allowed
+local to the sequence; ``g(h) = h // (N1 / N2)``; the band mask is aligned at
+the bottom-right corner as the causal mask is; a query row with no allowed
 key has ``O = 0`` and ``lse = +inf``; the fp32-rounded scale is used
 (``scale == 0`` means ``1/sqrt(D)``).
 
@@ -119,23 +131,49 @@ def selected_blocks(case, b: int, hs: int, qb: int, nkb_b: int, qbase_b: int):
     raise ValueError(kind)
 
 
-def _last_allowed_key(i: int, sq_b: int, skv_b: int, causal: bool) -> int:
-    """Largest key index query ``i`` may attend to: ``Skv-1``, or under the
-    bottom-right causal mask ``min(Skv-1, i + Skv - Sq)``."""
-    if causal:
-        return min(skv_b - 1, i + skv_b - sq_b)
-    return skv_b - 1
+def band_of(case):
+    """``(preTokens, nextTokens)`` of the case's band mask, or None."""
+    return getattr(case, "band", None)
+
+
+def allowed_key_range(i: int, sq_b: int, skv_b: int, case):
+    """Inclusive range ``[lo, hi]`` of keys query ``i`` may attend to before
+    the block selection: ``[0, Skv-1]``; under the bottom-right causal mask
+    ``hi = min(Skv-1, i + Skv - Sq)``; under the band mask
+    ``lo = max(0, i + Skv - Sq - preTokens)``,
+    ``hi = min(Skv-1, i + Skv - Sq + nextTokens)``.  Empty when ``lo > hi``."""
+    lo, hi = 0, skv_b - 1
+    off = skv_b - sq_b
+    band = band_of(case)
+    if band is not None:
+        pre, nxt = band
+        lo = max(lo, i + off - pre)
+        hi = min(hi, i + off + nxt)
+    elif case.causal:
+        hi = min(hi, i + off)
+    return lo, hi
 
 
 def visited_blocks(case, b, hs, qb, sq_b, skv_b, nkb_b, qbase_b):
     """``V``: the selected blocks holding at least one allowed (query, key)
-    pair for the rows of q-block ``qb``.  The allowed keys of a row form the
-    prefix ``[0, last_allowed_key(i)]``, which grows with ``i``, so a block is
-    visited when its first key is allowed for the q-block's last row."""
+    pair for the rows of q-block ``qb``.
+
+    Every row's allowed keys form one range (``allowed_key_range``), and the
+    range of row ``i + 1`` is that of row ``i`` moved up by one key (before
+    clipping to ``[0, Skv)``), holding ``preTokens + nextTokens + 1`` keys under
+    the band mask.  When that count is at least one, consecutive ranges meet,
+    so the union over the q-block's rows is the range from the first row's
+    lower end to the last row's upper end; a block is visited when it meets
+    that union.  When it is below one, no row has any key."""
     sel = selected_blocks(case, b, hs, qb, nkb_b, qbase_b)
+    band = band_of(case)
+    if band is not None and band[0] + band[1] < 0:
+        return []
+    first_row = qb * case.bx
     last_row = min((qb + 1) * case.bx, sq_b) - 1
-    lim = _last_allowed_key(last_row, sq_b, skv_b, case.causal)
-    return [kb for kb in sel if kb * case.by <= lim]
+    lo, _ = allowed_key_range(first_row, sq_b, skv_b, case)
+    _, hi = allowed_key_range(last_row, sq_b, skv_b, case)
+    return [kb for kb in sel if kb * case.by <= hi and min((kb + 1) * case.by, skv_b) - 1 >= lo]
 
 
 def _q_heads_of_sparse_head(case, hs):
@@ -240,11 +278,10 @@ def _row_problem(case, b, h, qb, sq, skv, nkb, qbase):
     keys = [np.arange(kb * case.by, min((kb + 1) * case.by, skv[b])) for kb in vis]
     keys = np.concatenate(keys) if keys else np.zeros(0, dtype=np.int64)
     i_loc = np.arange(i0, i1)
-    if case.causal:
-        lim = np.minimum(skv[b] - 1, i_loc + skv[b] - sq[b])
-    else:
-        lim = np.full(i_loc.shape, skv[b] - 1)
-    allowed = keys[None, :] <= lim[:, None]
+    rng = [allowed_key_range(int(i), sq[b], skv[b], case) for i in i_loc]
+    lo = np.array([r[0] for r in rng], dtype=np.int64)
+    hi = np.array([r[1] for r in rng], dtype=np.int64)
+    allowed = (keys[None, :] >= lo[:, None]) & (keys[None, :] <= hi[:, None])
     return i_loc, keys, allowed
 
 

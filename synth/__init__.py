@@ -124,6 +124,7 @@ class Case:
     v: np.ndarray
     dout_bits: Optional[np.ndarray] = None
     dout: Optional[np.ndarray] = None
+    band: Optional[tuple] = None  # (preTokens, nextTokens) of a band mask, or None
 
     # ---- derived shape facts (pure bookkeeping, no attention arithmetic) ----
     @property
@@ -368,13 +369,15 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 def random_case(seed: int, *, lens_q, lens_kv=None, N1=2, N2=None, D=64, dtype="bf16",
                 bx=128, by=128, kind="mask", sparse_heads=None, causal=False, paged=False,
                 page_size=128, density=0.5, width=None, scale=0.0, with_dout=True,
-                messy=False, rows=None, dense_q=False, out_dtype="") -> Case:
+                messy=False, rows=None, dense_q=False, out_dtype="", band=None) -> Case:
     """Random varlen case.
 
     ``messy`` adds duplicates, unsorted order, out-of-range entries and
     counts outside ``[0, W]`` to sabi/idx inputs (all of which the method
     must treat as set selection with out-of-range entries skipped).
     ``dense_q`` fills the mask/sabi/idx with every block (all-selected).
+    ``band`` = (preTokens, nextTokens) selects the band mask (``causal`` is
+    then ignored).
     """
     rng = np.random.default_rng(seed)
     N2 = N1 if N2 is None else N2
@@ -382,7 +385,9 @@ def random_case(seed: int, *, lens_q, lens_kv=None, N1=2, N2=None, D=64, dtype="
     lens_q = [int(x) for x in lens_q]
     lens_kv = list(lens_q) if lens_kv is None else [int(x) for x in lens_kv]
     B = len(lens_q)
-    c = _base(f"rand{seed}", dtype, B, N1, N2, D, bx, by, kind, hs, causal, paged, page_size, scale, out_dtype)
+    c = _base(f"rand{seed}", dtype, B, N1, N2, D, bx, by, kind, hs, causal and band is None, paged, page_size,
+              scale, out_dtype)
+    c["band"] = None if band is None else (int(band[0]), int(band[1]))
     c["cu_q"] = _cu(lens_q)
     nqb = [_cdiv(L, bx) for L in lens_q]
     nkb = [_cdiv(L, by) for L in lens_kv]

@@ -62,7 +62,13 @@ def token_allowed(case, b, h):
         for j in range(Skv):
             if (j // by) not in chosen:
                 continue
-            if case.causal and j > i + (Skv - Sq):
+            band = getattr(case, "band", None)
+            if band is not None:
+                # the window of query i: preTokens earlier and nextTokens later
+                # tokens around its bottom-right aligned diagonal key i + Skv - Sq
+                if j < i + (Skv - Sq) - band[0] or j > i + (Skv - Sq) + band[1]:
+                    continue
+            elif case.causal and j > i + (Skv - Sq):
                 continue
             A[i, j] = True
     return A

@@ -47,6 +47,17 @@ def tiny_cases():
     out.append(synth.random_case(17, lens_q=[21], lens_kv=[35], N1=3, N2=3, D=8, bx=8, by=8, kind="none"))
     out.append(synth.random_case(18, lens_q=[26, 19], N1=4, N2=2, D=8, bx=16, by=16, kind="sabi",
                                  sparse_heads=4, paged=True, page_size=16, causal=False))
+    # band masks (preTokens, nextTokens): a window around the diagonal with
+    # Sq != Skv, a one-key window, windows that exclude the diagonal (negative
+    # preTokens / nextTokens), paged GQA
+    out.append(synth.random_case(19, lens_q=[45, 30], lens_kv=[60, 22], N1=2, D=8, bx=16, by=16, kind="mask",
+                                 density=0.7, band=(20, 5)))
+    out.append(synth.random_case(20, lens_q=[33, 21], N1=4, N2=2, D=8, bx=8, by=16, kind="sabi", sparse_heads=2,
+                                 band=(0, 0), dense_q=True))
+    out.append(synth.random_case(21, lens_q=[40, 27], lens_kv=[52, 30], N1=2, N2=1, D=8, bx=16, by=8, kind="idx",
+                                 sparse_heads=1, paged=True, page_size=16, band=(-3, 12), messy=True))
+    out.append(synth.random_case(22, lens_q=[50], lens_kv=[31], N1=2, D=8, bx=16, by=16, kind="none",
+                                 band=(40, -2)))
     return out
 
 
@@ -180,6 +191,81 @@ def test_work_list_hand_example():
     assert idx["col_ptr"].tolist() == [0, 2, 3, 4, 5]
     assert idx["qrows"].tolist() == [0, 1, 2, 1, 1]
     assert idx["work_kv"].tolist() == [0, 1, 2, 3]
+
+
+def test_band_extremes_equal_causal_and_no_mask():
+    """A band with preTokens beyond every sequence and nextTokens = 0 is the
+    bottom-right causal mask; with both beyond every sequence it is no mask:
+    the same index products and the same outputs."""
+    kw = dict(lens_q=[37, 20, 44], lens_kv=[50, 20, 30], N1=2, D=8, bx=16, by=16, kind="mask", density=0.6)
+    causal = synth.random_case(31, causal=True, **kw)
+    band_c = synth.random_case(31, band=(10 ** 6, 0), **kw)
+    plain = synth.random_case(31, **kw)
+    band_n = synth.random_case(31, band=(10 ** 6, 10 ** 6), **kw)
+    for a, b in ((causal, band_c), (plain, band_n)):
+        ia, ib = oracle.index_products(a), oracle.index_products(b)
+        for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+            assert np.array_equal(ia[k], ib[k]), k
+        (Oa, la), (Ob, lb) = oracle.forward(a), oracle.forward(b)
+        assert np.array_equal(Oa, Ob) and np.array_equal(la, lb)
+
+
+def test_band_single_key_window_closed_form():
+    """preTokens = nextTokens = 0 leaves each query exactly one key, the
+    diagonal key j = i + Skv - Sq (when it exists and its block is selected):
+    O_i = v_j and lse_i = scale q_i . k_j; the other rows are empty."""
+    case = synth.random_case(32, lens_q=[30, 41], lens_kv=[45, 33], N1=2, D=8, bx=16, by=16, kind="mask",
+                             density=0.6, band=(0, 0))
+    O, lse = oracle.forward(case)
+    sg = oracle.scale_of(case.scale, case.D)
+    sq, skv = oracle.lengths(case)
+    for b in range(case.B):
+        for h in range(case.N1):
+            for i in range(sq[b]):
+                t = int(case.cu_q[b]) + i
+                j = i + skv[b] - sq[b]
+                sel = 0 <= j < skv[b] and case.sparse[b, h, i // 16, j // 16] != 0
+                if not sel:
+                    assert np.isinf(lse[t, h]) and np.all(O[t, h] == 0)
+                    continue
+                kj = case.k[int(case.cu_kv[b]) + j, h].astype(np.float64)
+                vj = case.v[int(case.cu_kv[b]) + j, h].astype(np.float64)
+                np.testing.assert_allclose(O[t, h], vj, rtol=0, atol=1e-12)
+                assert abs(lse[t, h] - sg * float(case.q[t, h].astype(np.float64) @ kj)) < 1e-12
+
+
+def test_band_empty_window():
+    """preTokens + nextTokens < 0: no query has a key -- every row is empty
+    (O = 0, lse = +inf), the index has no visited block, and the gradients
+    vanish."""
+    case = synth.random_case(33, lens_q=[40, 25], N1=2, D=8, bx=16, by=16, kind="none", band=(5, -7))
+    O, lse = oracle.forward(case)
+    assert np.all(O == 0) and np.all(np.isinf(lse))
+    idx = oracle.index_products(case)
+    assert idx["row_ptr"][-1] == 0 and len(idx["cols"]) == 0
+    dq, dk, dv = oracle.backward(case)
+    assert np.all(dq == 0) and np.all(dk == 0) and np.all(dv == 0)
+
+
+def test_band_dense_matches_torch_sdpa_window_mask():
+    """No block selection, Sq = Skv, band (pre, next): torch's SDPA in float64
+    with the boolean window mask j - pre <= ... written as a matrix."""
+    pre, nxt = 9, 4
+    case = synth.random_case(34, lens_q=[57, 33], N1=2, D=16, bx=16, by=16, kind="none", band=(pre, nxt))
+    O, lse = oracle.forward(case)
+    sg = oracle.scale_of(case.scale, case.D)
+    for b in range(case.B):
+        t0, t1 = int(case.cu_q[b]), int(case.cu_q[b + 1])
+        S = t1 - t0
+        i = np.arange(S)[:, None]
+        j = np.arange(S)[None, :]
+        m = torch.from_numpy((j >= i - pre) & (j <= i + nxt))
+        for h in range(case.N1):
+            q = torch.from_numpy(case.q[t0:t1, h].astype(np.float64))[None]
+            k = torch.from_numpy(case.k[t0:t1, h].astype(np.float64))[None]
+            v = torch.from_numpy(case.v[t0:t1, h].astype(np.float64))[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m[None], scale=sg)[0]
+            np.testing.assert_allclose(O[t0:t1, h], ref.numpy(), rtol=0, atol=1e-12)
 
 
 def test_causal_bottom_right_visited_blocks():
