@@ -384,14 +384,49 @@ struct Operands<L, D, false> {
   __device__ __forceinline__ int tr(int mt, int h) const { return tr_[mt][h]; }
 };
 
+// Compact per-lane offsets of the same two read patterns for an XorTile<D>
+// (3 registers instead of D/16 + D/16): the XOR permutation only moves the
+// chunk bits that kk (resp. mt) select, so the row-major read of step kk is
+// rb ^ 32 kk and the transposed read of feature tile mt, half h is
+// tb[h] ^ 64 mt (checked for every lane, step and tile at D = 64 and 128).
+// Each read then costs one XOR; refresh() keeps the compiler from hoisting
+// the XORs (one register per step) out of a loop.
+template <int D>
+struct XorOperands {
+  using L = XorTile<D>;
+  int rb, tb0, tb1;
+  __device__ __forceinline__ void init() {
+    const int lane = lane_id(), s16 = lane & 15;
+    rb = L::chunk_off(lane & 31, lane >> 5);
+    const int c0 = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    tb0 = L::col_off(4 * (lane >> 5) + (s16 >> 2), c0);
+    tb1 = L::col_off(4 * (lane >> 5) + (s16 >> 2) + 8, c0);
+  }
+  __device__ __forceinline__ void refresh() {
+    pin(rb);
+    pin(tb0);
+    pin(tb1);
+  }
+  __device__ __forceinline__ int rd(int kk) const { return rb ^ (32 * kk); }
+  __device__ __forceinline__ int tr(int mt, int h) const { return (h ? tb1 : tb0) ^ (64 * mt); }
+};
+
 // A/B operand (rows row0 + lane % 32) via ds_read_b128.
-template <class L, int D>
-__device__ __forceinline__ u32x4_t read_operand(const char* lds, const Operands<L, D>& of, int row0, int kk) {
+template <class L, class OF>
+__device__ __forceinline__ u32x4_t read_operand_of(const char* lds, const OF& of, int row0, int kk) {
   return lds_read16(lds + row0 * L::ROW_BYTES, of.rd(kk));
 }
-// A operand of the transposed tile for the 16-row chunk k0 = 16 kc, columns 32 mt ..
 template <class L, int D>
-__device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, const Operands<L, D>& of, int k0, int mt) {
+__device__ __forceinline__ u32x4_t read_operand(const char* lds, const Operands<L, D>& of, int row0, int kk) {
+  return read_operand_of<L>(lds, of, row0, kk);
+}
+template <int D>
+__device__ __forceinline__ u32x4_t read_operand(const char* lds, const XorOperands<D>& of, int row0, int kk) {
+  return read_operand_of<XorTile<D>>(lds, of, row0, kk);
+}
+// A operand of the transposed tile for the 16-row chunk k0 = 16 kc, columns 32 mt ..
+template <class L, class OF>
+__device__ __forceinline__ u32x4_t read_tr_operand_of(const char* lds, const OF& of, int k0, int mt) {
   const char* base = lds + k0 * L::ROW_BYTES;
   const u32x2_t lo = lds_read_tr(base, of.tr(mt, 0));
   const u32x2_t hi = lds_read_tr(base, of.tr(mt, 1));
@@ -401,6 +436,14 @@ __device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, const Operan
   r.z = hi.x;
   r.w = hi.y;
   return r;
+}
+template <class L, int D>
+__device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, const Operands<L, D>& of, int k0, int mt) {
+  return read_tr_operand_of<L>(lds, of, k0, mt);
+}
+template <int D>
+__device__ __forceinline__ u32x4_t read_tr_operand(const char* lds, const XorOperands<D>& of, int k0, int mt) {
+  return read_tr_operand_of<XorTile<D>>(lds, of, k0, mt);
 }
 
 // Runs N MFMA steps whose A (or B) operands come from LDS: step i's operand

@@ -180,17 +180,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 
 // ----------------------------------------------------------------- dK, dV --
 // Work item: one 128-key tile of KV block (g, b, kb), taken by a workgroup of
-// two waves; wave w owns keys 64 w .. 64 w + 63 as two 32-key tiles and keeps
-// their K and V rows in registers as the B operands of S = Q K^T and
-// dP = dO V^T.  For every q-head of the group and every q-block in the tile's
-// transposed list, 64-row query sub-tiles of Q, dO, lse and D are staged
-// through double-buffered LDS and each wave computes, per 32-row half,
+// NW waves; wave w owns NT 32-key tiles (keys 32 NT w ..) and keeps their K
+// and V rows in registers as the B operands of S = Q K^T and dP = dO V^T.  For
+// every q-head of the group and every q-block in the tile's transposed list,
+// 64-row query sub-tiles of Q, dO, lse and D are staged through
+// double-buffered LDS and each wave computes, per 32-row half,
 //   S, dP                (MFMA, Q / dO row-major from LDS)
 //   P = exp2(S scale log2e - lse log2e), dS = P o (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (Q^T / dO^T via LDS transpose loads,
 //                                      P / dS straight from registers)
-// Every operand read from LDS feeds the MFMAs of both key tiles; dK and dV
-// accumulate in AGPRs.
+// Every operand read from LDS feeds the MFMAs of the wave's NT key tiles; dK
+// and dV accumulate in AGPRs.
 constexpr int QS = 64;  // query rows per staged sub-tile
 
 // Walk over (q-head of the group, q-block of the tile's column list, 64-row
@@ -239,17 +239,31 @@ struct ColWalk {
   __device__ __forceinline__ int row_end() const { return min((ldu(qrows, e) + 1) * bx, sq); }
 };
 
-constexpr int DKDV_WAVES = 2;   // a workgroup's waves, 64 keys each
+// Workgroup shape of the dK/dV kernel: NW waves of NT 32-key tiles.  Two
+// waves of 64 keys, two workgroups per CU (one wave per SIMD): each Q / dO
+// operand read from LDS feeds two MFMAs.  Four waves of 32 keys (two waves
+// per SIMD, so one wave's softmax could hide behind the other's MFMAs) need
+// ~280 registers at D = 128 against the 256 a wave then gets; the spilled
+// build was 22 % slower, so both head dims use the 64-key waves.
+template <int D>
+struct DkdvShape {
+  static constexpr int NT = 2, NW = 2, LOOK = 4;
+};
+constexpr int DKDV_KEYS = 128;  // keys per work item
 constexpr int DKDV_STAGES = 2;  // LDS ring depth (two workgroups per CU share the LDS)
 
 template <typename MF, int D, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 1) void k_bwd_dkdv(BwdArgs a) {
+  constexpr int NT = DkdvShape<D>::NT;
+  constexpr int NW = DkdvShape<D>::NW;
+  constexpr int LOOK = DkdvShape<D>::LOOK;  // MFMA operands read this many steps ahead
+  static_assert(32 * NT * NW == DKDV_KEYS, "a workgroup covers the 128-key tile");
   using QL = XorTile<D>;  // Q and dO: read row-major (S, dP) and transposed (dK^T, dV^T)
   constexpr int TILE = QL::template bytes<QS>();
   constexpr int STAGE = 2 * TILE + 2 * QS * 4;  // Q, dO, lse, D
   constexpr int NMT = D / 32;
   constexpr int NKK = D / 16;
-  using Dma = DmaXor<D, QS, DKDV_WAVES>;
+  using Dma = DmaXor<D, QS, NW>;
   __shared__ __attribute__((aligned(16))) char smem[DKDV_STAGES * STAGE];
 
   const int KVI = ldu(a.hdr, H_KVITEMS);
@@ -274,11 +288,11 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     kv0 = ldu(a.seq.cu_kv, b);
     skv = (int)(ldu(a.seq.cu_kv, b + 1) - kv0);
   }
-  const int key_lo = kb * a.seq.by + sub * 128;
+  const int key_lo = kb * a.seq.by + sub * DKDV_KEYS;
   if (key_lo >= skv) return;
   const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // this lane's keys: column lane % 32 of the wave's two 32-key tiles
-  const int key_w = key_lo + 64 * wv + (lane & 31);
+  // this lane's keys: column lane % 32 of the wave's 32-key tiles
+  const int key_w = key_lo + 32 * NT * wv + (lane & 31);
   const int qoff = skv - sq;
   const int64_t kvstride = (int64_t)a.n2 * D;
   // element offset of key `key` (< skv) of this tile, head g, column 0
@@ -290,9 +304,9 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
       return (kv0 + key) * kvstride + (int64_t)g * D;
     }
   };
-  u32x4_t kf[2][NKK], vf[2][NKK];
+  u32x4_t kf[NT][NKK], vf[NT][NKK];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < NT; ++n) {
     const int key = key_w + 32 * n;
     const int64_t krow = (PAGED && key >= skv ? 0 : key_row(key)) + 8 * (lane >> 5);
 #pragma unroll
@@ -301,9 +315,9 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
       vf[n][kk] = key < skv ? gload16(reinterpret_cast<const uint16_t*>(a.v) + krow + 16 * kk) : zero_u4();
     }
   }
-  f32x16_t dk[2][NMT], dv[2][NMT];
+  f32x16_t dk[NT][NMT], dv[NT][NMT];
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       dk[n][mt] = zero16();
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
 
   Dma dma;
   dma.init(qstride);
-  Operands<QL, D> of;
+  XorOperands<D> of;
   of.init();
   auto issue = [&](int stage) {
     char* st = smem + stage * STAGE;
@@ -352,7 +366,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     dma.issue(st + TILE, dop + off, nvalid);
     float* stat = reinterpret_cast<float*>(st + 2 * TILE);
     // lse (wave 0) and -D (wave 1) of the tile's rows
-    dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.ndl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
+    if (wv < 2) dma_rows_f32(stat + wv * QS, (wv == 0 ? a.lse2 : a.ndl) + (q0 + r0) * a.n1 + h, a.n1, nvalid);
     ld.next();
   };
 
@@ -363,10 +377,11 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     const int r0 = r0_next;            // the tile computed in this step
     const int nrows = rend_next - r0;  // its rows inside the q-block and the sequence (may exceed QS)
     wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // both waves' loads landed; the other stage is no longer read
+    __builtin_amdgcn_s_barrier();  // every wave's loads landed; the other stage is no longer read
     more = ld.valid();
     if (more) issue(stage ^ 1);
     settle_scalar_loads();
+    of.refresh();
     char* ql = smem + stage * STAGE;
     char* dl_ = ql + TILE;
     const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
@@ -374,11 +389,11 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
 
     // Rows past the q-block or sequence end, or keys above some row's causal
     // limit, need masks; every other tile takes the mask-free path.
-    const bool masked = nrows < QS || (CAUSAL && key_lo + 127 > r0 + qoff);
+    const bool masked = nrows < QS || (CAUSAL && key_lo + DKDV_KEYS - 1 > r0 + qoff);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
       // dP starts from -D of each element's row, so the MFMAs leave dP - D
-      f32x16_t s[2], dp[2];
+      f32x16_t s[NT], dp[NT];
       {
         f32x16_t ndt;
 #pragma unroll
@@ -388,16 +403,16 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
           for (int j = 0; j < 4; ++j) ndt[4 * ig + j] = __uint_as_float(d4[j]);
         }
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
+        for (int n = 0; n < NT; ++n) {
           s[n] = zero16();
           dp[n] = ndt;
         }
       }
-      // S, dP of rows 32 h .. + 31: each Q / dO operand read feeds both key tiles
-      mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * h, i >> 1); },
+      // S, dP of rows 32 h .. + 31: each Q / dO operand read feeds the NT key tiles
+      mfma_pipeline<2 * NKK, LOOK>([&](int i) { return read_operand((i & 1) ? dl_ : ql, of, 32 * h, i >> 1); },
                                 [&](int i, const u32x4_t& op) {
 #pragma unroll
-                                  for (int n = 0; n < 2; ++n) {
+                                  for (int n = 0; n < NT; ++n) {
                                     if (i & 1)
                                       dp[n] = MF::mfma(op, vf[n][i >> 1], dp[n]);
                                     else
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
                                   }
                                 });
       // P = exp2(S scale log2e - lse log2e), dS = P o (dP - D)
-      u32x4_t pb[2][2], db[2][2];
+      u32x4_t pb[NT][2], db[NT][2];
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         const int rl = 32 * h + 8 * ig + 4 * (lane >> 5);  // first of 4 consecutive query rows
@@ -414,7 +429,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * ig + j;
 #pragma unroll
-          for (int n = 0; n < 2; ++n) {
+          for (int n = 0; n < NT; ++n) {
             const float p = fast_exp2(fmaf(s[n][i], c2, -__uint_as_float(l4[j])));
             s[n][i] = p;
             dp[n][i] *= p;
@@ -426,7 +441,7 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 #pragma unroll
-          for (int n = 0; n < 2; ++n) {
+          for (int n = 0; n < NT; ++n) {
             if ((CAUSAL && key_w + 32 * n > r0 + rl + qoff) || rl >= nrows) {
               s[n][i] = 0.f;
               dp[n][i] = 0.f;
@@ -435,21 +450,21 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < NT; ++n) {
         pb[n][0] = pack8<MF>(s[n], 0);
         pb[n][1] = pack8<MF>(s[n], 8);
         db[n][0] = pack8<MF>(dp[n], 0);
         db[n][1] = pack8<MF>(dp[n], 8);
       }
       // dV^T += dO^T P, dK^T += Q^T dS over the 16-row chunks 2 h, 2 h + 1;
-      // each transposed operand read feeds both key tiles
-      mfma_pipeline<4 * NMT, 4>(
+      // each transposed operand read feeds the NT key tiles
+      mfma_pipeline<4 * NMT, LOOK>(
           [&](int i) { return read_tr_operand((i & 1) ? ql : dl_, of, 16 * (2 * h + i / (2 * NMT)), (i >> 1) % NMT); },
           [&](int i, const u32x4_t& op) {
             const int c = i / (2 * NMT);
             const int mt = (i >> 1) % NMT;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+            for (int n = 0; n < NT; ++n) {
               if (i & 1)
                 MF::mfma_acc(dk[n][mt], op, db[n][c]);
               else
@@ -459,12 +474,13 @@ __global__ __launch_bounds__(64 * DKDV_WAVES, 1) void k_bwd_dkdv(BwdArgs a) {
     }
     stage ^= 1;
   }
-  mfma_acc_done(dk[0]);
-  mfma_acc_done(dk[1]);
-  mfma_acc_done(dv[0]);
-  mfma_acc_done(dv[1]);
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < NT; ++n) {
+    mfma_acc_done(dk[n]);
+    mfma_acc_done(dv[n]);
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
     const int key = key_w + 32 * n;
     if (key < skv) {
       const int64_t orow = key_row(key);
@@ -493,10 +509,11 @@ hipError_t launch_dq_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
 }
 template <typename MF, int D, bool PAGED>
 hipError_t launch_dkdv_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
+  constexpr unsigned threads = 64 * DkdvShape<D>::NW;
   if (a.seq.causal)
-    k_bwd_dkdv<MF, D, true, PAGED><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
+    k_bwd_dkdv<MF, D, true, PAGED><<<(unsigned)grid, threads, 0, st>>>(a);
   else
-    k_bwd_dkdv<MF, D, false, PAGED><<<(unsigned)grid, 64 * DKDV_WAVES, 0, st>>>(a);
+    k_bwd_dkdv<MF, D, false, PAGED><<<(unsigned)grid, threads, 0, st>>>(a);
   return hipGetLastError();
 }
 template <typename MF, int D>
