@@ -31,7 +31,7 @@ BSA_ERR_RUNTIME = 561000
 
 BSA_DTYPE_F16, BSA_DTYPE_BF16, BSA_DTYPE_FP8_E4M3 = 1, 2, 3
 BSA_SPARSE_NONE, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_SABI_U16, BSA_SPARSE_IDX_I32 = 0, 1, 2, 3
-BSA_MASK_NONE, BSA_MASK_CAUSAL = 0, 1
+BSA_MASK_NONE, BSA_MASK_CAUSAL, BSA_MASK_BAND = 0, 1, 2
 BSA_KV_TND, BSA_KV_PAGED = 0, 1
 BSA_FLAG_INDEX_BUILT = 1
 (BSA_KERNEL_INDEX, BSA_KERNEL_FWD, BSA_KERNEL_BWD_PRE, BSA_KERNEL_BWD_DKDV, BSA_KERNEL_BWD_DQ) = range(5)
@@ -69,6 +69,8 @@ class bsa_problem_t(ctypes.Structure):
         ("scale", ctypes.c_double),
         ("flags", ctypes.c_uint32),
         ("out_dtype", ctypes.c_int32),
+        ("pre_tokens", ctypes.c_int64),
+        ("next_tokens", ctypes.c_int64),
     ]
 
 

@@ -72,7 +72,8 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
   if (p->sparse_heads != p->num_heads_q && p->sparse_heads != p->num_heads_kv) return BSA_ERR_PARAM_INVALID;
   if (p->sparse_kind != BSA_SPARSE_NONE && (p->sparse_rows < 0 || p->sparse_width < 1)) return BSA_ERR_PARAM_INVALID;
   if (p->sparse_kind == BSA_SPARSE_IDX_I32 && p->sparse_width > 256) return BSA_ERR_PARAM_INVALID;
-  if (p->mask_type != BSA_MASK_NONE && p->mask_type != BSA_MASK_CAUSAL) return BSA_ERR_PARAM_INVALID;
+  if (p->mask_type != BSA_MASK_NONE && p->mask_type != BSA_MASK_CAUSAL && p->mask_type != BSA_MASK_BAND)
+    return BSA_ERR_PARAM_INVALID;
   if (p->kv_layout != BSA_KV_TND && p->kv_layout != BSA_KV_PAGED) return BSA_ERR_PARAM_INVALID;
   if (p->kv_layout == BSA_KV_PAGED) {
     const int64_t row = (int64_t)p->num_heads_kv * p->head_dim;
@@ -210,7 +211,15 @@ SeqArgs make_seq(const bsa_problem_t* p, const int64_t* cu_q, const int64_t* cu_
   s.batch = p->batch;
   s.bx = p->block_x;
   s.by = p->block_y;
-  s.causal = p->mask_type == BSA_MASK_CAUSAL;
+  s.masked = p->mask_type != BSA_MASK_NONE;
+  auto clampw = [](int64_t x) { return (int32_t)std::max<int64_t>(-WIN_INF, std::min<int64_t>(WIN_INF, x)); };
+  if (p->mask_type == BSA_MASK_BAND) {
+    s.win_lo = -clampw(p->pre_tokens);
+    s.win_hi = clampw(p->next_tokens);
+  } else {
+    s.win_lo = -WIN_INF;
+    s.win_hi = 0;
+  }
   return s;
 }
 

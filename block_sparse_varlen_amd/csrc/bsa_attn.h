@@ -253,19 +253,25 @@ struct RegTileWalk {
   // The caller waits for the initial load (any vmcnt wait covering it) before
   // the first take<false>(); take<true>() reads its entry with a scalar load
   // instead, for a first sub-tile issued before that wait.
-  __device__ __forceinline__ void init(const int32_t* c, int e0, int e_end, int by_, int kend_) {
+  // kstart: the item's smallest allowed key (its first row's band start, 0
+  // without a band); sub-tiles that end below it are skipped.
+  __device__ __forceinline__ void init(const int32_t* c, int e0, int e_end, int by_, int kend_, int kstart = 0) {
     cols = c;
-    e = e0;
     e1 = e_end;
     // the list is ascending: drop trailing blocks that start at or past kend
     // (only a slice of a q-block taller than 128 rows can end before the
     // q-block's causal limit, so this loop rarely runs)
     while (e1 > e0 && ldu(c, e1 - 1) * by_ >= kend_) --e1;
+    // and leading blocks that end below kstart (band masks only)
+    while (e0 < e1 && (ldu(c, e0) + 1) * by_ <= kstart) ++e0;
+    e = e0;
     base = e0;
     s = 0;
     by = by_;
     nsub = by_ / T;
     kend = kend_;
+    // first sub-tile of the first block that reaches kstart
+    if (kstart > 0 && e0 < e1) s = max(0, (kstart - ldu(c, e0) * by_) / T);
     colv = e0 + lane_id() < e_end ? c[e0 + lane_id()] : 0;
   }
   __device__ __forceinline__ bool valid() const { return e < e1; }

@@ -53,9 +53,9 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 //   P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T o (dP^T - D)
 //   dQ^T += K^T dS^T                       (K^T via LDS transpose loads)
 // The dP^T accumulator starts from -D (a loop-invariant register tile), and
-// key masks run only on sub-tiles that reach past Skv or the causal limit.
+// key masks run only on sub-tiles that reach past Skv or outside a row's window.
 
-template <typename MF, int D, bool CAUSAL, bool PAGED>
+template <typename MF, int D, bool WIN, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   using L = XorTile<D>;  // K: read row-major (S^T) and transposed (dQ^T); V: row-major (dP^T)
   constexpr int TILE = L::template bytes<KT>();
@@ -75,9 +75,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   // a wave whose 32 rows all lie past the item's rows only helps with the
   // copies and the barriers
   const bool wave_active = wv * 32 < it.nrows;
+  // with a token window (causal or band mask) key j is allowed for row i when
+  // i + qoff + win_lo <= j <= i + qoff + win_hi
   const int qoff = it.skv - it.sq;
-  int kend = it.skv;
-  if (CAUSAL) kend = min(kend, it.row_lo + it.nrows - 1 + qoff + 1);
+  const int win_lo = a.seq.win_lo, win_hi = a.seq.win_hi;
+  int kend = it.skv, kstart = 0;
+  if (WIN) {
+    kend = min(kend, it.row_lo + it.nrows - 1 + qoff + win_hi + 1);
+    kstart = max(0, it.row_lo + qoff + win_lo);
+  }
 
   const int64_t qstride = (int64_t)a.n1 * D;
   const int64_t tok = it.q0 + my_row;
@@ -103,7 +109,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) acc[mt] = zero16();
   const float c2 = a.sigma_log2e;
-  const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
+  const int lim = WIN ? min(it.skv - 1, my_row + qoff + win_hi) : it.skv - 1;
+  const int lo = WIN ? my_row + qoff + win_lo : 0;
 
   Dma dma;
   dma.init(a.n2 * D);
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   // `ld` walks the sub-tiles and loads each one a step before it is computed
   // (LDS double buffer); key_next is the first key of the last one issued
   RegTileWalk<> ld;
-  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
+  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend, kstart);
   KvAddr<PAGED> kva;
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   int key_next = 0;
@@ -140,7 +147,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     }
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
-    const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
+    const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
+    const bool edge = key0 + KT > it.skv || (WIN && (key0 + KT - 1 > rw0 + win_hi || key0 < rw0 + 31 + win_lo));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // 32-key halves of the sub-tile
       f32x16_t s = zero16(), dp = ndt;
@@ -154,11 +162,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
                                 });
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], c2, -lse2));
-      if (edge) {  // keys past Skv or above this row's causal limit
+      if (edge) {  // keys past Skv or outside this row's window
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (key > lim) s[i] = 0.f;
+          if (key > lim || key < lo) s[i] = 0.f;
         }
       }
 #pragma unroll
@@ -196,17 +204,20 @@ constexpr int QS = 64;  // query rows per staged sub-tile
 // Walk over (q-head of the group, q-block of the tile's column list, 64-row
 // part of the q-block: ceil(block_x / 64) of them, the last one short when
 // block_x is not a multiple of 64), skipping parts past the sequence end or
-// entirely above the causal limit of the tile's first key.
+// whose rows' windows miss the tile.
 struct ColWalk {
   const int32_t* col_ptr;
   const int32_t* qrows;
   int hh, e, e1, half;
-  int group, per_head, g, tkb, kg, sq, qoff, key_min, causal, bx, halves;  // halves = ceil(bx / QS)
+  int group, per_head, g, tkb, kg, sq, qoff, key_min, key_max, win, win_lo, win_hi, bx, halves;  // halves = ceil(bx / QS)
   __device__ __forceinline__ int col(int h) const { return (per_head ? g * group + h : g) * tkb + kg; }
+  // a part is skipped when its last row's window ends below the tile's first
+  // key or its first row's window starts above the tile's last key
   __device__ __forceinline__ bool ok(int qb, int hf) const {
     const int r0 = qb * bx + hf * QS;
     if (r0 >= sq) return false;
-    if (causal && min(min(r0 + QS, (qb + 1) * bx), sq) - 1 + qoff < key_min) return false;
+    if (win && min(min(r0 + QS, (qb + 1) * bx), sq) - 1 + qoff + win_hi < key_min) return false;
+    if (win && r0 + qoff + win_lo > key_max) return false;
     return true;
   }
   __device__ __forceinline__ void open(int h) {
@@ -252,7 +263,7 @@ struct DkdvShape {
 constexpr int DKDV_KEYS = 128;  // keys per work item
 constexpr int DKDV_STAGES = 2;  // LDS ring depth (two workgroups per CU share the LDS)
 
-template <typename MF, int D, bool CAUSAL, bool PAGED>
+template <typename MF, int D, bool WIN, bool PAGED>
 __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 1) void k_bwd_dkdv(BwdArgs a) {
   constexpr int NT = DkdvShape<D>::NT;
   constexpr int NW = DkdvShape<D>::NW;
@@ -294,6 +305,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
   // this lane's keys: column lane % 32 of the wave's 32-key tiles
   const int key_w = key_lo + 32 * NT * wv + (lane & 31);
   const int qoff = skv - sq;
+  const int win_lo = a.seq.win_lo, win_hi = a.seq.win_hi;
   const int64_t kvstride = (int64_t)a.n2 * D;
   // element offset of key `key` (< skv) of this tile, head g, column 0
   auto key_row = [&](int key) -> int64_t {
@@ -341,7 +353,10 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
   ld.sq = sq;
   ld.qoff = qoff;
   ld.key_min = key_lo;
-  ld.causal = CAUSAL;
+  ld.key_max = min(key_lo + DKDV_KEYS, skv) - 1;
+  ld.win = WIN;
+  ld.win_lo = a.seq.win_lo;
+  ld.win_hi = a.seq.win_hi;
   ld.bx = a.seq.bx;
   ld.halves = (a.seq.bx + QS - 1) / QS;
   ld.hh = 0;
@@ -387,9 +402,10 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
     const float* lsel = reinterpret_cast<const float*>(ql + 2 * TILE);
     const float* ndll = lsel + QS;
 
-    // Rows past the q-block or sequence end, or keys above some row's causal
-    // limit, need masks; every other tile takes the mask-free path.
-    const bool masked = nrows < QS || (CAUSAL && key_lo + DKDV_KEYS - 1 > r0 + qoff);
+    // Rows past the q-block or sequence end, or keys outside some row's
+    // window, need masks; every other tile takes the mask-free path.
+    const bool masked = nrows < QS || (WIN && (key_lo + DKDV_KEYS - 1 > r0 + qoff + win_hi ||
+                                               key_lo < r0 + QS - 1 + qoff + win_lo));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
       // dP starts from -D of each element's row, so the MFMAs leave dP - D
@@ -436,13 +452,14 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
           }
         }
       }
-      if (masked) {  // edge tiles only: P = dS = 0 past the sequence end or the causal limit
+      if (masked) {  // edge tiles only: P = dS = 0 past the sequence end or outside the window
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            if ((CAUSAL && key_w + 32 * n > r0 + rl + qoff) || rl >= nrows) {
+            const int kd = key_w + 32 * n - (r0 + rl + qoff);  // key minus the row's diagonal key
+            if ((WIN && (kd > win_hi || kd < win_lo)) || rl >= nrows) {
               s[n][i] = 0.f;
               dp[n][i] = 0.f;
             }
@@ -497,7 +514,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 
 template <typename MF, int D, bool PAGED>
 hipError_t launch_dq_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.seq.causal)
+  if (a.seq.masked)
     k_bwd_dq<MF, D, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
   else
     k_bwd_dq<MF, D, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
@@ -510,7 +527,7 @@ hipError_t launch_dq_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
 template <typename MF, int D, bool PAGED>
 hipError_t launch_dkdv_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
   constexpr unsigned threads = 64 * DkdvShape<D>::NW;
-  if (a.seq.causal)
+  if (a.seq.masked)
     k_bwd_dkdv<MF, D, true, PAGED><<<(unsigned)grid, threads, 0, st>>>(a);
   else
     k_bwd_dkdv<MF, D, false, PAGED><<<(unsigned)grid, threads, 0, st>>>(a);

@@ -35,7 +35,7 @@ namespace {
 // lse; only the rounding differs.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <typename MF, int D, bool CAUSAL, bool PAGED>
+template <typename MF, int D, bool WIN, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   // K is read row-major only (XOR-permuted chunks), V transposed only (rows
   // padded by 64 bytes): both layouts keep their read pattern conflict free
@@ -59,9 +59,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   // a wave whose 32 rows all lie past the item's rows (short q-blocks, the
   // sequence end) only helps with the copies and the barriers
   const bool wave_active = wv * 32 < it.nrows;
-  const int qoff = it.skv - it.sq;             // causal: key j allowed for row i when j <= i + qoff
-  int kend = it.skv;
-  if (CAUSAL) kend = min(kend, it.row_lo + it.nrows - 1 + qoff + 1);
+  // with a token window (causal or band mask) key j is allowed for row i when
+  // i + qoff + win_lo <= j <= i + qoff + win_hi
+  const int qoff = it.skv - it.sq;
+  const int win_lo = a.seq.win_lo, win_hi = a.seq.win_hi;
+  int kend = it.skv, kstart = 0;
+  if (WIN) {
+    kend = min(kend, it.row_lo + it.nrows - 1 + qoff + win_hi + 1);
+    kstart = max(0, it.row_lo + qoff + win_lo);
+  }
 
   // Q^T operand (B of S^T = K Q^T): lane holds row my_row, d = 16 kk + 8 (lane / 32) .. + 7
   const int64_t qstride = (int64_t)a.n1 * D;
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   // `ld` walks the sub-tiles and loads each one a step before it is computed
   // (LDS double buffer); key_next is the first key of the last one issued
   RegTileWalk<> ld;
-  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
+  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend, kstart);
   KvAddr<PAGED> kva;
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   int key_next = 0;
@@ -130,16 +136,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     // step i: kk = i / 2, key tile t = i % 2
     mfma_pipeline<2 * NKK, 4>([&](int i) { return read_operand(kl, ofk, 32 * (i & 1), i >> 1); },
                               [&](int i, const u32x4_t& op) { s[i & 1] = MF::mfma(op, qf[i >> 1], s[i & 1]); });
-    // ---- masks: keys past Skv, causal limit (edge sub-tiles only) ----
-    const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
+    // ---- masks: keys past Skv, outside the rows' windows (edge sub-tiles only) ----
+    const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
+    const bool edge = key0 + KT > it.skv || (WIN && (key0 + KT - 1 > rw0 + win_hi || key0 < rw0 + 31 + win_lo));
     if (edge) {
-      const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
+      const int lim = WIN ? min(it.skv - 1, my_row + qoff + win_hi) : it.skv - 1;
+      const int lo = WIN ? my_row + qoff + win_lo : 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (key > lim) s[t][i] = -INFINITY;
+          if (key > lim || key < lo) s[t][i] = -INFINITY;
         }
     }
     // ---- online softmax (row = this lane's column) ----
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 
 template <typename MF, int D, bool PAGED>
 hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.seq.causal)
+  if (a.seq.masked)
     k_fwd<MF, D, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
   else
     k_fwd<MF, D, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);

@@ -55,7 +55,7 @@ __device__ __forceinline__ int pack4_f8(float x0, float x1, float x2, float x3) 
 
 // Three workgroups per CU (three waves per SIMD: 168 registers each, 32 KiB
 // of LDS per workgroup); two measured 7 % slower.
-template <typename OUT, bool CAUSAL, bool PAGED>
+template <typename OUT, bool WIN, bool PAGED>
 __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   constexpr int D = 128;         // features (bytes per row)
   using L = XorTile<64>;         // 128-byte rows, 8 XOR-permuted 16-byte chunks
@@ -73,9 +73,15 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   const int my_row = it.row_lo + my_local;     // row within the sequence
   const bool row_ok = my_local < it.nrows;
   const bool wave_active = wv * 32 < it.nrows;
+  // with a token window (causal or band mask) key j is allowed for row i when
+  // i + qoff + win_lo <= j <= i + qoff + win_hi
   const int qoff = it.skv - it.sq;
-  int kend = it.skv;
-  if (CAUSAL) kend = min(kend, it.row_lo + it.nrows - 1 + qoff + 1);
+  const int win_lo = a.seq.win_lo, win_hi = a.seq.win_hi;
+  int kend = it.skv, kstart = 0;
+  if (WIN) {
+    kend = min(kend, it.row_lo + it.nrows - 1 + qoff + win_hi + 1);
+    kstart = max(0, it.row_lo + qoff + win_lo);
+  }
 
   // Q^T operand (B of S^T): lane holds its row's bytes 64 kk + 32 h .. + 31
   const int64_t qstride = (int64_t)a.n1 * D;  // bytes
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   kdma.init(a.n2 * (D / 2));
   vdma.init(a.n2 * (D / 2));
   RegTileWalk<> ld;
-  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend);
+  ld.init(a.cols, ldu(a.row_ptr, it.r), ldu(a.row_ptr, it.r + 1), a.seq.by, kend, kstart);
   KvAddr<PAGED> kva;
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D / 2, a.page_size, a.max_pages, a.page_stride / 2);
   int key_next = 0;
@@ -167,16 +173,18 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
       s[0] = mfma_f8(kop[1][0], qf[1], s[0]);
       s[1] = mfma_f8(kop[1][1], qf[1], s[1]);
     }
-    // ---- masks: keys past Skv, causal limit (edge sub-tiles only) ----
-    const bool edge = key0 + KT > it.skv || (CAUSAL && key0 + KT - 1 > it.row_lo + wv * 32 + qoff);
+    // ---- masks: keys past Skv, outside the rows' windows (edge sub-tiles only) ----
+    const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
+    const bool edge = key0 + KT > it.skv || (WIN && (key0 + KT - 1 > rw0 + win_hi || key0 < rw0 + 31 + win_lo));
     if (edge) {
-      const int lim = CAUSAL ? min(it.skv - 1, my_row + qoff) : it.skv - 1;
+      const int lim = WIN ? min(it.skv - 1, my_row + qoff + win_hi) : it.skv - 1;
+      const int lo = WIN ? my_row + qoff + win_lo : 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * hl + (i & 3);
-          if (key > lim) s[t][i] = -INFINITY;
+          if (key > lim || key < lo) s[t][i] = -INFINITY;
         }
     }
     // ---- online softmax (row = this lane's column) ----
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
 
 template <typename OUT, bool PAGED>
 hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.seq.causal)
+  if (a.seq.masked)
     k_fwd_fp8<OUT, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
   else
     k_fwd_fp8<OUT, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);

@@ -8,7 +8,8 @@
 //    one allowed (query, key) pair -- the selected set (block mask, 0xFFFF
 //    padded sabi, or -1 padded idx with count; BlockSparseAttentionGrad README,
 //    BlitzSparseAttention sabi section, GenericBlockSparseAttention parameter
-//    table) de-duplicated, restricted to [0, nKB_b) and cut by the causal mask;
+//    table) de-duplicated, restricted to [0, nKB_b) and cut by the causal or
+//    band mask;
 //  * work: rows by visited count descending, ties by row id (longest first for
 //    load balance, the role of GenericBlockSparseAttention's metadata
 //    pre-operator);
@@ -110,17 +111,27 @@ __global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs
 __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, const IndexPtrs& ip,
                           int r, int R, int TQB) {
   const int lane = lane_id();
-  int nbits = 0, b = 0, qb = 0, hs = 0, qg = 0;
+  int nbits = 0, kb_lo = 0, b = 0, qb = 0, hs = 0, qg = 0;
   if (r < R) {
     hs = r / TQB;
     qg = r - hs * TQB;
     b = ip.qb_seq[qg];
     qb = qg - ip.qbase[b];
     const int sq = ip.sq[b], skv = ip.skv[b];
+    const int first_row = qb * seq.bx;
     const int last_row = min((qb + 1) * seq.bx, sq) - 1;
+    // The rows' allowed key ranges slide up by one key per row, so their
+    // union is [first row's lower end, last row's upper end]; an empty
+    // window (win_lo > win_hi) leaves no key at all.
     int lim = skv - 1;  // largest allowed key of the q-block's last row
-    if (seq.causal) lim = min(lim, last_row + skv - sq);
-    nbits = lim < 0 ? 0 : lim / seq.by + 1;
+    int lo = 0;         // smallest allowed key of its first row
+    if (seq.masked) {
+      lim = min(lim, last_row + skv - sq + seq.win_hi);
+      lo = max(lo, first_row + skv - sq + seq.win_lo);
+      if (seq.win_lo > seq.win_hi) lim = -1;
+    }
+    nbits = lim < lo ? 0 : lim / seq.by + 1;
+    kb_lo = lim < lo ? 0 : lo / seq.by;
   }
   const int nwords = (nbits + 31) >> 5;
   for (int w = lane; w < nwords; w += 64) {
@@ -128,6 +139,11 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
     if (sel.kind == SP_NONE) {
       const int hi = nbits - w * 32;
       v = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+      const int lb = kb_lo - w * 32;  // blocks below kb_lo hold no allowed key
+      if (lb >= 32)
+        v = 0;
+      else if (lb > 0)
+        v &= ~((1u << lb) - 1u);
     }
     bm[w] = v;
   }
@@ -139,13 +155,13 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
         if (sel.kind == SP_MASK) {
           const uint8_t* m = reinterpret_cast<const uint8_t*>(sel.sparse) + row;
           const int n = min(sel.width, nbits);
-          for (int kb = lane; kb < n; kb += 64)
+          for (int kb = kb_lo + lane; kb < n; kb += 64)
             if (m[kb]) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
         } else {
           const uint16_t* s = reinterpret_cast<const uint16_t*>(sel.sparse) + row;
           for (int t = lane; t < sel.width; t += 64) {
             const int kb = s[t];
-            if (kb != 0xFFFF && kb < nbits) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+            if (kb != 0xFFFF && kb < nbits && kb >= kb_lo) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
           }
         }
       }
@@ -156,7 +172,7 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
         const int32_t* ix = reinterpret_cast<const int32_t*>(sel.sparse) + rr * sel.width;
         for (int t = lane; t < n; t += 64) {
           const int kb = ix[t];
-          if (kb >= 0 && kb < nbits) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+          if (kb >= kb_lo && kb < nbits) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
         }
       }
     }

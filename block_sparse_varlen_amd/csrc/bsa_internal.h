@@ -57,8 +57,16 @@ struct SeqArgs {
   const int32_t* seqused_kv;  // paged keys, or nullptr
   int32_t batch;
   int32_t bx, by;
-  int32_t causal;
+  // Token window of the causal and band masks: key j is allowed for query i
+  // when i + (Skv - Sq) + win_lo <= j <= i + (Skv - Sq) + win_hi (no window:
+  // masked = 0).  Causal: win_lo = -WIN_INF, win_hi = 0; band: -preTokens,
+  // nextTokens, both clamped to [-WIN_INF, WIN_INF].
+  int32_t masked;
+  int32_t win_lo, win_hi;
 };
+// Any window edge at or beyond this many tokens acts as unbounded (sequence
+// lengths stay below 2^28, so i + (Skv - Sq) + win never overflows int32).
+constexpr int32_t WIN_INF = 1 << 30;
 
 struct SelArgs {
   const void* sparse;

@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 from . import (
-    BSA_DTYPE_BF16, BSA_DTYPE_F16, BSA_DTYPE_FP8_E4M3, BSA_KV_PAGED, BSA_KV_TND, BSA_MASK_CAUSAL, BSA_MASK_NONE,
+    BSA_DTYPE_BF16, BSA_DTYPE_F16, BSA_DTYPE_FP8_E4M3, BSA_KV_PAGED, BSA_KV_TND, BSA_MASK_BAND, BSA_MASK_CAUSAL,
+    BSA_MASK_NONE,
     BSA_FLAG_INDEX_BUILT, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_IDX_I32, BSA_SPARSE_NONE, BSA_SPARSE_SABI_U16,
     bsa_build_index, bsa_bwd, bsa_fwd, bsa_get_workspace_size, bsa_index_view, problem,
 )
@@ -29,6 +30,11 @@ def problem_for(case):
     else:
         lens_kv = np.diff(case.cu_kv)
     sp = case.sparse
+    band = getattr(case, "band", None)
+    if band is not None:
+        mask = dict(mask_type=BSA_MASK_BAND, pre_tokens=int(band[0]), next_tokens=int(band[1]))
+    else:
+        mask = dict(mask_type=BSA_MASK_CAUSAL if case.causal else BSA_MASK_NONE)
     return problem(
         dtype=_DTYPE[case.dtype],
         out_dtype=_DTYPE[case.out_dtype] if getattr(case, "out_dtype", "") else 0,
@@ -40,12 +46,12 @@ def problem_for(case):
         sparse_heads=case.sparse_heads,
         sparse_rows=int(sp.shape[-2]) if sp is not None else 0,
         sparse_width=int(sp.shape[-1]) if sp is not None else 0,
-        mask_type=BSA_MASK_CAUSAL if case.causal else BSA_MASK_NONE,
         kv_layout=BSA_KV_PAGED if case.paged else BSA_KV_TND,
         page_size=case.page_size if case.paged else 0,
         max_pages_per_seq=int(case.block_table.shape[1]) if case.paged else 0,
         page_stride=case.page_size * case.N2 * case.D if case.paged else 0,
         scale=float(case.scale),
+        **mask,
     )
 
 

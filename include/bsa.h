@@ -18,7 +18,13 @@
  *   (b) j < Skv_b, and
  *   (c) with BSA_MASK_CAUSAL, j <= i + Skv_b - Sq_b (causal mask aligned at
  *       the bottom-right corner, the FlashAttention UnpaddingScoreGradV2
- *       page's rightDownCausal, the only causal mode of its TND layout).
+ *       page's rightDownCausal, the only causal mode of its TND layout);
+ *       with BSA_MASK_BAND, i + Skv_b - Sq_b - pre_tokens <= j <=
+ *       i + Skv_b - Sq_b + next_tokens (the band, sparseMode 4, of the
+ *       FlashAttention UnpaddingScoreGradV2 page, section 6.6, and the
+ *       BlitzSparseAttention page's sparseMode limits, aligned at the same
+ *       corner; preTokens / nextTokens count the earlier / later tokens the
+ *       sliding window keeps, PromptFlashAttention page, attribute table).
  * A row with no allowed key gets O = 0 and lse = +inf; in the backward pass
  * its dQ is 0, and keys no row reaches get dK = dV = 0.
  *
@@ -94,7 +100,13 @@ enum {
   BSA_SPARSE_IDX_I32 = 3
 };
 
-enum { BSA_MASK_NONE = 0, BSA_MASK_CAUSAL = 1 };
+/* Token masks.  BSA_MASK_BAND reads pre_tokens / next_tokens; either may be
+   negative (a window that leaves out the diagonal key), and a window with
+   pre_tokens + next_tokens < 0 holds no key.  Values beyond 2^30 in size act
+   as unbounded: BAND with pre_tokens >= 2^30 and next_tokens = 0 is CAUSAL.
+   GenericBlockSparseAttention's planned window mask (winLeft / winRight) is
+   the same band. */
+enum { BSA_MASK_NONE = 0, BSA_MASK_CAUSAL = 1, BSA_MASK_BAND = 2 };
 
 /* K/V layout: packed [T_kv, N2, D] rows addressed through cu_seqlens_kv, or
    paged [pages, page_size, N2, D] through block_table + seqused_kv
@@ -138,6 +150,8 @@ typedef struct bsa_problem {
   double scale;              /* > 0, or 0 for 1/sqrt(D); applied rounded to fp32 */
   uint32_t flags;            /* BSA_FLAG_* bits, others must be 0 */
   int32_t out_dtype;         /* 0 (= dtype) or dtype for fp16 / bf16; F16 or BF16 with FP8_E4M3 inputs */
+  int64_t pre_tokens;        /* BSA_MASK_BAND: earlier tokens the window keeps (else ignored) */
+  int64_t next_tokens;       /* BSA_MASK_BAND: later tokens the window keeps (else ignored) */
 } bsa_problem_t;
 
 /* Stage 1.  Checks `p` and writes the workspace bytes bsa_fwd (`fwd_bytes`)

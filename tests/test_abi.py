@@ -29,7 +29,9 @@ def test_every_declared_function_is_exported():
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(bsa.bsa_problem_t) == 112
+    assert ctypes.sizeof(bsa.bsa_problem_t) == 128
+    assert bsa.bsa_problem_t.pre_tokens.offset == 112
+    assert bsa.bsa_problem_t.next_tokens.offset == 120
     assert bsa.bsa_problem_t.total_q.offset == 24
     assert bsa.bsa_problem_t.page_stride.offset == 88
     assert bsa.bsa_problem_t.scale.offset == 96
@@ -49,6 +51,15 @@ def status(p, fwd=True, bwd=True):
     b = ctypes.c_size_t(0)
     return bsa.library().bsa_get_workspace_size(ctypes.byref(p) if p is not None else None,
                                                 ctypes.byref(f) if fwd else None, ctypes.byref(b) if bwd else None)
+
+
+def test_band_mask_accepted():
+    """BSA_MASK_BAND with any pre / next tokens (negative ones included) is a
+    valid descriptor; the window does not change the workspace bounds."""
+    f0, b0 = bsa.bsa_get_workspace_size(good())
+    for pre, nxt in ((128, 0), (-5, 40), (2 ** 40, -(2 ** 40)), (0, 0)):
+        f, b = bsa.bsa_get_workspace_size(good(mask_type=bsa.BSA_MASK_BAND, pre_tokens=pre, next_tokens=nxt))
+        assert (f, b) == (f0, b0)
 
 
 def test_workspace_size_ok():
@@ -72,7 +83,7 @@ def test_workspace_size_ok():
     (dict(sparse_kind=7), bsa.BSA_ERR_PARAM_INVALID),
     (dict(sparse_heads=3), bsa.BSA_ERR_PARAM_INVALID),
     (dict(sparse_kind=bsa.BSA_SPARSE_IDX_I32, sparse_width=300), bsa.BSA_ERR_PARAM_INVALID),
-    (dict(mask_type=2), bsa.BSA_ERR_PARAM_INVALID),
+    (dict(mask_type=3), bsa.BSA_ERR_PARAM_INVALID),
     (dict(scale=-1.0), bsa.BSA_ERR_PARAM_INVALID),
     (dict(scale=float("nan")), bsa.BSA_ERR_PARAM_INVALID),
     (dict(flags=2), bsa.BSA_ERR_PARAM_INVALID),  # unknown flag bit

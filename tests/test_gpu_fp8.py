@@ -36,6 +36,9 @@ def cases():
         # a large scale: frequent moves of the reference maximum (P stays <= 256)
         "mask_scale08": R(408, lens_q=[400, 300], N1=2, kind="mask", scale=0.8, density=0.7, out_dtype="bf16",
                           **F),
+        # band mask with Sq != Skv
+        "sabi_band_f16": R(409, lens_q=[450, 200], lens_kv=[520, 330], N1=2, kind="sabi", band=(150, 30),
+                           dense_q=True, out_dtype="f16", **F),
     }
 
 

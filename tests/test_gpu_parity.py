@@ -98,6 +98,21 @@ def fwd_cases():
         "mask_bx1024_by1024": R(126, lens_q=[2500, 1100], N1=2, D=64, kind="mask", bx=1024, by=1024, density=0.7),
         "sabi_bx1024_by1024_causal": R(127, lens_q=[2100, 1500], N1=2, D=128, kind="sabi", bx=1024, by=1024,
                                        causal=True),
+        # band masks (preTokens, nextTokens): windows narrower and wider than a
+        # block, Sq != Skv, windows that leave out the diagonal, an empty
+        # window, paged GQA, tall q-blocks, one-token q-blocks
+        "none_band_300_40": R(128, lens_q=[700, 333], N1=2, D=128, kind="none", band=(300, 40)),
+        "mask_band_37_5_sqskv": R(129, lens_q=[520, 300], lens_kv=[800, 260], N1=2, D=64, kind="mask",
+                                  density=0.8, band=(37, 5)),
+        "sabi_band_neg_pre_gqa": R(130, lens_q=[400, 260], N1=4, N2=2, D=128, kind="sabi", sparse_heads=2,
+                                   band=(-20, 150), dense_q=True),
+        "idx_band_paged_f16": R(131, lens_q=[610, 390], lens_kv=[700, 500], N1=4, N2=2, D=128, dtype="f16",
+                                kind="idx", sparse_heads=2, paged=True, band=(129, -3), dense_q=True),
+        "none_band_empty_window": R(132, lens_q=[300, 150], N1=2, D=64, kind="none", band=(4, -9)),
+        "mask_band_bx256_by256": R(133, lens_q=[900, 530], N1=2, D=128, kind="mask", bx=256, by=256,
+                                   density=0.9, band=(600, 0)),
+        "none_band_bx1_by64": R(134, lens_q=[90, 40], lens_kv=[500, 200], N1=2, D=64, kind="none", bx=1, by=64,
+                                band=(70, 10)),
     }
 
 
@@ -158,6 +173,19 @@ def bwd_cases():
         "mask_bx1024_by1024": R(225, lens_q=[2500, 1100], N1=2, D=64, kind="mask", bx=1024, by=1024, density=0.7),
         "sabi_bx1024_by1024_causal_f16": R(226, lens_q=[2100, 1500], N1=2, D=128, dtype="f16", kind="sabi",
                                            bx=1024, by=1024, causal=True),
+        # band masks
+        "none_band_300_40": R(227, lens_q=[700, 333], N1=2, D=128, kind="none", band=(300, 40)),
+        "mask_band_37_5_sqskv_f16": R(228, lens_q=[520, 300], lens_kv=[800, 260], N1=2, D=64, dtype="f16",
+                                      kind="mask", density=0.8, band=(37, 5)),
+        "sabi_band_neg_pre_gqa_perhead": R(229, lens_q=[400, 260], N1=4, N2=2, D=128, kind="sabi", sparse_heads=4,
+                                           band=(-20, 150), dense_q=True),
+        "idx_band_paged": R(230, lens_q=[610, 390], lens_kv=[700, 500], N1=4, N2=2, D=128, kind="idx",
+                            sparse_heads=2, paged=True, band=(129, -3), dense_q=True),
+        "none_band_empty_window": R(231, lens_q=[300, 150], N1=2, D=64, kind="none", band=(4, -9)),
+        "mask_band_bx256_by256": R(232, lens_q=[900, 530], N1=2, D=128, kind="mask", bx=256, by=256,
+                                   density=0.9, band=(600, 0)),
+        "none_band_bx16_sq_gt_skv": R(233, lens_q=[300, 200], lens_kv=[180, 260], N1=2, D=128, kind="none", bx=16,
+                                      band=(90, 20)),
     }
 
 
