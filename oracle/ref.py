@@ -18,7 +18,11 @@ approximation), with the passage each part follows:
   ``blockSparseMaskOptional``), uint16 sabi padded with 0xFFFF
   (BlitzSparseAttention page, sabi section), int32 sparseBlockIdx/Count padded
   with -1 over global q-blocks (GenericBlockSparseAttention page, parameter
-  table and "Blocking and addressing" constraint).
+  table and "Blocking and addressing" constraint), and the other
+  layoutSparsePattern forms of the same page's table: per-Q-block lists with a
+  batch axis (values 0 / 2), and per-KV-block lists -- each KV block names
+  the q-blocks that chose it -- over global KV blocks (5 / 7) or with a batch
+  axis (1 / 3).
 * Varlen ``cu_seqlens`` with a leading 0 and ``seqused_kv`` for the paged
   layout; paged K/V ``[pages, page_size, N2, D]`` addressed through a block
   table (GenericBlockSparseAttention page, parameter table, "Paged Attention").
@@ -128,7 +132,43 @@ def selected_blocks(case, b: int, hs: int, qb: int, nkb_b: int, qbase_b: int):
         W = sp.shape[2]
         n = min(max(int(case.count[hs, gq]), 0), W)
         return sorted({int(x) for x in sp[hs, gq, :n] if 0 <= int(x) < nkb_b})
+    if kind == "idx_b":  # [B, Hs, maxQBlocks, W], local q-blocks
+        if qb >= sp.shape[2]:
+            return []
+        W = sp.shape[3]
+        n = min(max(int(case.count[b, hs, qb]), 0), W)
+        return sorted({int(x) for x in sp[b, hs, qb, :n] if 0 <= int(x) < nkb_b})
+    if kind in ("kvidx", "kvidx_b"):
+        # per-KV-block lists: kb is selected for q-block qb when qb is among
+        # the first clamp(count, 0, W) entries of kb's list
+        chosen = []
+        for kb in range(nkb_b):
+            lst = kv_list(case, b, hs, kb)
+            if qb in lst:
+                chosen.append(kb)
+        return chosen
     raise ValueError(kind)
+
+
+def kv_list(case, b: int, hs: int, kb: int):
+    """The q-blocks (local to sequence ``b``) that KV block ``kb`` of sparse
+    head ``hs`` lists, as a set: the first ``clamp(count, 0, W)`` entries; list
+    rows past the tensor's row dimension list nothing.  ``kvidx`` holds
+    ``[Hs, totalKBlocks, W]`` over global KV blocks ``kbase_b + kb``
+    (layoutSparsePattern 5 / 7), ``kvidx_b`` ``[B, Hs, maxKvBlocks, W]``
+    (layoutSparsePattern 1 / 3)."""
+    sp, cnt = case.sparse, case.count
+    if case.sparse_kind == "kvidx":
+        _, _, _, _, _, kbase = _blocking(case)
+        gk = kbase[b] + kb
+        if gk >= sp.shape[1]:
+            return set()
+        n = min(max(int(cnt[hs, gk]), 0), sp.shape[2])
+        return {int(x) for x in sp[hs, gk, :n]}
+    if kb >= sp.shape[2]:
+        return set()
+    n = min(max(int(cnt[b, hs, kb]), 0), sp.shape[3])
+    return {int(x) for x in sp[b, hs, kb, :n]}
 
 
 def band_of(case):

@@ -16,7 +16,11 @@ Conventions (shared by every consumer):
   (BlitzSparseAttention page, "sabi block-sparse index" section).
 * idx/count: int32 ``[Hs, totalQBlocks, W]`` padded with -1 and int32
   ``[Hs, totalQBlocks]`` (GenericBlockSparseAttention page,
-  ``sparseBlockIdx`` / ``sparseBlockCount``).
+  ``sparseBlockIdx`` / ``sparseBlockCount``, layoutSparsePattern 4 / 6);
+  the table's other layouts: ``idx_b`` ``[B, Hs, maxQBlocks, W]`` (0 / 2),
+  ``kvidx`` ``[Hs, totalKBlocks, W]`` listing q-blocks per KV block (5 / 7),
+  ``kvidx_b`` ``[B, Hs, maxKvBlocks, W]`` (1 / 3), each with its count
+  tensor of the leading shape.
 * Paged K/V: ``[pages, page_size, N2, D]`` with an int32 ``block_table``
   ``[B, max_pages]`` padded with -1 (GenericBlockSparseAttention page,
   "Paged Attention" table).
@@ -449,6 +453,50 @@ def random_case(seed: int, *, lens_q, lens_kv=None, N1=2, N2=None, D=64, dtype="
                         n_cnt = int(rng.integers(-1, W + 3))
                     cnt[h, base + j] = n_cnt
             base += nqb[b]
+        c["sparse"] = idx
+        c["count"] = cnt
+    elif kind in ("idx_b", "kvidx", "kvidx_b"):
+        # idx_b: [B, Hs, rows, W] lists of KV blocks per local q-block;
+        # kvidx: [Hs, totalKBlocks, W] lists of local q-blocks per global KV
+        # block; kvidx_b: [B, Hs, rows, W] the same per local KV block
+        per_kv = kind != "idx_b"
+        lists_n = nkb if per_kv else nqb  # lists per sequence
+        pools = nqb if per_kv else nkb    # what a list's entries index
+        Wd = max(max(pools) if B else 1, 1)
+        W = Wd if width is None else width
+        if kind == "kvidx":
+            tkb = int(sum(nkb))
+            idx = np.full((hs, tkb, W), -1, dtype=np.int32)
+            cnt = np.zeros((hs, tkb), dtype=np.int32)
+        else:
+            Rl = max(max(lists_n) if B else 1, 1) if rows is None else rows
+            idx = np.full((B, hs, Rl, W), -1, dtype=np.int32)
+            cnt = np.zeros((B, hs, Rl), dtype=np.int32)
+        base = 0
+        for b in range(B):
+            for j in range(lists_n[b]):
+                for h in range(hs):
+                    pool = max(pools[b], 1)
+                    if dense_q:
+                        sel = np.arange(min(pool, W))
+                    else:
+                        n = int(rng.integers(0, min(pool, W) + 1))
+                        sel = np.sort(rng.choice(pool, n, replace=False))
+                    if messy:
+                        extra = rng.integers(-2, pool + 3, size=int(rng.integers(0, 3)))
+                        sel = np.concatenate([sel, extra])
+                        rng.shuffle(sel)
+                        sel = sel[:W]
+                    n_cnt = len(sel)
+                    if messy and rng.random() < 0.2:
+                        n_cnt = int(rng.integers(-1, W + 3))
+                    if kind == "kvidx":
+                        idx[h, base + j, :len(sel)] = sel
+                        cnt[h, base + j] = n_cnt
+                    elif j < idx.shape[2]:
+                        idx[b, h, j, :len(sel)] = sel
+                        cnt[b, h, j] = n_cnt
+            base += lists_n[b]
         c["sparse"] = idx
         c["count"] = cnt
     elif kind != "none":

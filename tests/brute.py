@@ -59,6 +59,34 @@ def token_allowed(case, b, h):
                     val = int(idx[hs, gq, t])
                     if val >= 0:
                         chosen.add(val)
+        elif case.sparse_kind == "idx_b":
+            idx, cnt = case.sparse, case.count
+            if qb < idx.shape[2]:
+                n = int(cnt[b, hs, qb])
+                n = 0 if n < 0 else min(n, idx.shape[3])
+                for t in range(n):
+                    val = int(idx[b, hs, qb, t])
+                    if val >= 0:
+                        chosen.add(val)
+        elif case.sparse_kind in ("kvidx", "kvidx_b"):
+            # key block kb is chosen for this query's block when kb's own
+            # list of query blocks contains it
+            idx, cnt = case.sparse, case.count
+            gk0 = sum(-(-skv[x] // by) for x in range(b))
+            for kb in range(-(-Skv // by)):
+                if case.sparse_kind == "kvidx":
+                    if gk0 + kb >= idx.shape[1]:
+                        continue
+                    n = int(cnt[hs, gk0 + kb])
+                    lst = idx[hs, gk0 + kb]
+                else:
+                    if kb >= idx.shape[2]:
+                        continue
+                    n = int(cnt[b, hs, kb])
+                    lst = idx[b, hs, kb]
+                n = 0 if n < 0 else min(n, len(lst))
+                if qb in [int(x) for x in lst[:n]]:
+                    chosen.add(kb)
         for j in range(Skv):
             if (j // by) not in chosen:
                 continue

@@ -58,6 +58,17 @@ def tiny_cases():
                                  sparse_heads=1, paged=True, page_size=16, band=(-3, 12), messy=True))
     out.append(synth.random_case(22, lens_q=[50], lens_kv=[31], N1=2, D=8, bx=16, by=16, kind="none",
                                  band=(40, -2)))
+    # the other layoutSparsePattern forms: per-Q-block lists with a batch axis,
+    # per-KV-block lists over global KV blocks and with a batch axis (messy
+    # entries, counts out of range, fewer list rows than KV blocks)
+    out.append(synth.random_case(23, lens_q=[37, 20, 44], lens_kv=[50, 9, 30], N1=4, N2=2, D=8, bx=16, by=8,
+                                 kind="idx_b", sparse_heads=2, messy=True, causal=True))
+    out.append(synth.random_case(24, lens_q=[45, 0, 33], lens_kv=[40, 12, 52], N1=4, N2=2, D=8, bx=8, by=16,
+                                 kind="kvidx", sparse_heads=4, messy=True, paged=True, page_size=16))
+    out.append(synth.random_case(25, lens_q=[60, 28], lens_kv=[64, 70], N1=2, D=8, bx=16, by=8, kind="kvidx_b",
+                                 messy=True, causal=True, rows=6))
+    out.append(synth.random_case(26, lens_q=[41, 30], N1=2, N2=1, D=8, bx=16, by=16, kind="kvidx",
+                                 sparse_heads=1, band=(12, 3)))
     return out
 
 
@@ -191,6 +202,84 @@ def test_work_list_hand_example():
     assert idx["col_ptr"].tolist() == [0, 2, 3, 4, 5]
     assert idx["qrows"].tolist() == [0, 1, 2, 1, 1]
     assert idx["work_kv"].tolist() == [0, 1, 2, 3]
+
+
+def _kv_lists_from_mask(mask_case, kind):
+    """The mask case's selection rewritten as per-KV-block lists: KV block kb
+    of sequence b lists every q-block whose mask row selects it (the
+    layoutSparsePattern table's "each KV block lists the Q blocks that chose
+    it"), in ascending order, padded with -1."""
+    c = copy.copy(mask_case)
+    sq, skv = oracle.lengths(mask_case)
+    nqb = [-(-s // mask_case.bx) for s in sq]
+    nkb = [-(-s // mask_case.by) for s in skv]
+    Hs, W = mask_case.sparse_heads, max(nqb)
+    lists = {}
+    for b in range(mask_case.B):
+        for hs in range(Hs):
+            for kb in range(nkb[b]):
+                lists[b, hs, kb] = [qb for qb in range(nqb[b])
+                                    if kb < mask_case.sparse.shape[3] and mask_case.sparse[b, hs, qb, kb]]
+    if kind == "kvidx":
+        idx = np.full((Hs, sum(nkb), W), -1, dtype=np.int32)
+        cnt = np.zeros((Hs, sum(nkb)), dtype=np.int32)
+        for (b, hs, kb), lst in lists.items():
+            idx[hs, sum(nkb[:b]) + kb, :len(lst)] = lst
+            cnt[hs, sum(nkb[:b]) + kb] = len(lst)
+    else:
+        idx = np.full((mask_case.B, Hs, max(nkb), W), -1, dtype=np.int32)
+        cnt = np.zeros((mask_case.B, Hs, max(nkb)), dtype=np.int32)
+        for (b, hs, kb), lst in lists.items():
+            idx[b, hs, kb, :len(lst)] = lst
+            cnt[b, hs, kb] = len(lst)
+    c.sparse_kind, c.sparse, c.count = kind, idx, cnt
+    return c, lists
+
+
+@pytest.mark.parametrize("kind", ["kvidx", "kvidx_b"])
+def test_kv_lists_equal_their_per_q_block_transpose(kind):
+    """Per-KV-block lists made from a block mask select exactly what the mask
+    selects: identical index products and outputs; and without a token mask
+    the transposed lists the index builds (col_ptr / qrows) are the input
+    lists themselves."""
+    m = synth.random_case(35, lens_q=[70, 33, 50], lens_kv=[60, 40, 81], N1=4, N2=2, D=8, bx=16, by=16,
+                          kind="mask", sparse_heads=4, density=0.5)
+    c, lists = _kv_lists_from_mask(m, kind)
+    im, ic = oracle.index_products(m), oracle.index_products(c)
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+        assert np.array_equal(im[k], ic[k]), k
+    (Om, lm), (Oc, lc) = oracle.forward(m), oracle.forward(c)
+    assert np.array_equal(Om, Oc) and np.array_equal(lm, lc)
+    sq, skv = oracle.lengths(m)
+    nkb = [-(-s // 16) for s in skv]
+    TKB = sum(nkb)
+    for (b, hs, kb), lst in lists.items():
+        col = hs * TKB + sum(nkb[:b]) + kb
+        assert list(ic["qrows"][ic["col_ptr"][col]:ic["col_ptr"][col + 1]]) == lst
+
+
+def test_batch_major_idx_equals_global_idx():
+    """The same per-Q-block lists laid out [B, Hs, maxQBlocks, W]
+    (layoutSparsePattern 0 / 2) and [Hs, totalQBlocks, W] (4 / 6) select the
+    same blocks."""
+    g = synth.random_case(36, lens_q=[70, 33, 50], lens_kv=[60, 40, 81], N1=4, N2=2, D=8, bx=16, by=16,
+                          kind="idx", sparse_heads=2, messy=True)
+    sq, _ = oracle.lengths(g)
+    nqb = [-(-s // 16) for s in sq]
+    Hs, W = g.sparse.shape[0], g.sparse.shape[2]
+    idx = np.full((g.B, Hs, max(nqb), W), -1, dtype=np.int32)
+    cnt = np.zeros((g.B, Hs, max(nqb)), dtype=np.int32)
+    for b in range(g.B):
+        for q in range(nqb[b]):
+            idx[b, :, q] = g.sparse[:, sum(nqb[:b]) + q]
+            cnt[b, :, q] = g.count[:, sum(nqb[:b]) + q]
+    c = copy.copy(g)
+    c.sparse_kind, c.sparse, c.count = "idx_b", idx, cnt
+    ig, ic = oracle.index_products(g), oracle.index_products(c)
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+        assert np.array_equal(ig[k], ic[k]), k
+    (Og, lg), (Oc, lc) = oracle.forward(g), oracle.forward(c)
+    assert np.array_equal(Og, Oc) and np.array_equal(lg, lc)
 
 
 def test_band_extremes_equal_causal_and_no_mask():
