@@ -31,6 +31,7 @@ BSA_ERR_RUNTIME = 561000
 
 BSA_DTYPE_F16, BSA_DTYPE_BF16, BSA_DTYPE_FP8_E4M3 = 1, 2, 3
 BSA_SPARSE_NONE, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_SABI_U16, BSA_SPARSE_IDX_I32 = 0, 1, 2, 3
+BSA_SPARSE_IDX_BATCH_I32, BSA_SPARSE_KV_IDX_I32, BSA_SPARSE_KV_IDX_BATCH_I32 = 4, 5, 6
 BSA_MASK_NONE, BSA_MASK_CAUSAL, BSA_MASK_BAND = 0, 1, 2
 BSA_KV_TND, BSA_KV_PAGED = 0, 1
 BSA_FLAG_INDEX_BUILT = 1

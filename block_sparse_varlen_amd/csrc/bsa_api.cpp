@@ -68,10 +68,11 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
   if (p->num_heads_q < 1 || p->num_heads_q > 256 || p->num_heads_kv < 1) return BSA_ERR_PARAM_INVALID;
   if (p->num_heads_q % p->num_heads_kv != 0 || p->num_heads_q / p->num_heads_kv > 128) return BSA_ERR_PARAM_INVALID;
   if (p->block_x <= 0 || p->block_y <= 0 || p->block_y % 16 != 0) return BSA_ERR_PARAM_INVALID;
-  if (p->sparse_kind < BSA_SPARSE_NONE || p->sparse_kind > BSA_SPARSE_IDX_I32) return BSA_ERR_PARAM_INVALID;
+  if (p->sparse_kind < BSA_SPARSE_NONE || p->sparse_kind > BSA_SPARSE_KV_IDX_BATCH_I32) return BSA_ERR_PARAM_INVALID;
   if (p->sparse_heads != p->num_heads_q && p->sparse_heads != p->num_heads_kv) return BSA_ERR_PARAM_INVALID;
   if (p->sparse_kind != BSA_SPARSE_NONE && (p->sparse_rows < 0 || p->sparse_width < 1)) return BSA_ERR_PARAM_INVALID;
-  if (p->sparse_kind == BSA_SPARSE_IDX_I32 && p->sparse_width > 256) return BSA_ERR_PARAM_INVALID;
+  if ((p->sparse_kind == BSA_SPARSE_IDX_I32 || p->sparse_kind == BSA_SPARSE_IDX_BATCH_I32) && p->sparse_width > 256)
+    return BSA_ERR_PARAM_INVALID;
   if (p->mask_type != BSA_MASK_NONE && p->mask_type != BSA_MASK_CAUSAL && p->mask_type != BSA_MASK_BAND)
     return BSA_ERR_PARAM_INVALID;
   if (p->kv_layout != BSA_KV_TND && p->kv_layout != BSA_KV_PAGED) return BSA_ERR_PARAM_INVALID;
@@ -114,13 +115,18 @@ Bounds make_bounds(const bsa_problem_t* p) {
   b.rbar = (int64_t)p->sparse_heads * b.qbar;
   b.cbar = (int64_t)p->sparse_heads * b.kbar;
   const int64_t nkb = std::max<int32_t>(b.nkb_max, 1);
-  b.cmax = (int32_t)(p->sparse_kind == BSA_SPARSE_NONE ? nkb : std::min<int64_t>(p->sparse_width, nkb));
+  // per-KV-block lists may select every KV block for one q-block
+  const bool all_kb = p->sparse_kind == BSA_SPARSE_NONE || kv_lists(p->sparse_kind);
+  b.cmax = (int32_t)(all_kb ? nkb : std::min<int64_t>(p->sparse_width, nkb));
   b.nnzbar = std::max<int64_t>(b.rbar * b.cmax, 1);
   b.kvbar = (int64_t)p->num_heads_kv * b.kbar;
   const int group = p->num_heads_q / p->num_heads_kv;
   b.kvkey_max = (p->sparse_heads == p->num_heads_q ? group : 1) * std::max<int32_t>(b.nqb_max, 1);
   return b;
 }
+
+// 32-bit words of one row's visited-block bitmap
+int64_t kv_words(const Bounds& b) { return std::max<int64_t>((b.nkb_max + 31) / 32, 1); }
 
 bool bounds_fit(const Bounds& b) {
   const int64_t lim = (int64_t)1 << 30;
@@ -157,6 +163,8 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   // one radix sort's histograms, or both work lists' side by side
   L.hist = take((size_t)(256 * (cdiv64(b.rbar, 256) + cdiv64(b.kvbar, 256)) + 2) * 4);
   L.work = take((size_t)b.rbar * 4);
+  // per-KV-block lists are scattered into per-row bitmaps first
+  L.kvbm = kv_lists(p->sparse_kind) ? take((size_t)b.rbar * kv_words(b) * 4) : 0;
   if (with_csc) {
     L.col_cnt = take((size_t)b.cbar * 4);
     L.col_ptr = take((size_t)(b.cbar + 1) * 4);
@@ -223,8 +231,13 @@ SeqArgs make_seq(const bsa_problem_t* p, const int64_t* cu_q, const int64_t* cu_
   return s;
 }
 
-SelArgs make_sel(const bsa_problem_t* p, const void* sparse, const int32_t* count) {
+SelArgs make_sel(const bsa_problem_t* p, const void* sparse, const int32_t* count, void* ws, const Layout& L,
+                 const Bounds& b) {
   SelArgs s{};
+  if (kv_lists(p->sparse_kind)) {
+    s.kvbm = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.kvbm);
+    s.kv_words = (int32_t)kv_words(b);
+  }
   s.sparse = sparse;
   s.count = count;
   s.kind = p->sparse_kind;
@@ -245,7 +258,7 @@ bsa_status_t check_index_ptrs(const bsa_problem_t* p, const int64_t* cu_q, const
   if (p->kv_layout == BSA_KV_TND && !cu_kv) return BSA_ERR_PARAM_NULLPTR;
   if (p->kv_layout == BSA_KV_PAGED && !seqused) return BSA_ERR_PARAM_NULLPTR;
   if (p->sparse_kind != BSA_SPARSE_NONE && !sparse) return BSA_ERR_PARAM_NULLPTR;
-  if (p->sparse_kind == BSA_SPARSE_IDX_I32 && !count) return BSA_ERR_PARAM_NULLPTR;
+  if (p->sparse_kind >= BSA_SPARSE_IDX_I32 && !count) return BSA_ERR_PARAM_NULLPTR;
   return BSA_OK;
 }
 
@@ -317,7 +330,7 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
   hipError_t e = hipSuccess;
   if (!(p->flags & BSA_FLAG_INDEX_BUILT)) {
     prof_begin(BSA_KERNEL_INDEX, s);
-    e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, false, s);
+    e = launch_index(seq, make_sel(p, sparse, count, workspace, L, b), b, ip, p->num_heads_kv, group, false, s);
     prof_end(BSA_KERNEL_INDEX, s);
     if (e != hipSuccess) return BSA_ERR_RUNTIME;
   }
@@ -440,7 +453,7 @@ bsa_status_t bsa_build_index(const bsa_problem_t* p, const int64_t* cu_q, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const IndexPtrs ip = make_ptrs(workspace, L, with_csc != 0);
   prof_begin(BSA_KERNEL_INDEX, s);
-  const hipError_t e = launch_index(make_seq(p, cu_q, cu_kv, seqused), make_sel(p, sparse, count), b, ip,
+  const hipError_t e = launch_index(make_seq(p, cu_q, cu_kv, seqused), make_sel(p, sparse, count, workspace, L, b), b, ip,
                                     p->num_heads_kv, p->num_heads_q / p->num_heads_kv, with_csc != 0, s);
   prof_end(BSA_KERNEL_INDEX, s);
   return from_hip(e);
@@ -502,7 +515,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   hipError_t e = hipSuccess;
   if (!(p->flags & BSA_FLAG_INDEX_BUILT)) {
     prof_begin(BSA_KERNEL_INDEX, s);
-    e = launch_index(seq, make_sel(p, sparse, count), b, ip, p->num_heads_kv, group, true, s);
+    e = launch_index(seq, make_sel(p, sparse, count, workspace, L, b), b, ip, p->num_heads_kv, group, true, s);
     prof_end(BSA_KERNEL_INDEX, s);
     if (e != hipSuccess) return BSA_ERR_RUNTIME;
   }

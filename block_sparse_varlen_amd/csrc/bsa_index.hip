@@ -21,6 +21,8 @@
 // whose results do not depend on order, the scans are sequential per block,
 // orders come from a stable LSD radix sort, and column lists are re-sorted
 // through bitmaps after their order-dependent atomic fill.
+#include <algorithm>
+
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -58,9 +60,16 @@ __device__ int block_incl_scan(int x, int* wsum, int& total) {
 // ------------------------------------------------------------------ setup --
 // One block: per-sequence lengths, q/kv block bases, block -> sequence maps,
 // header.
-__global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs, int n2) {
+// Blocks past the first clear the per-KV-block lists' bitmap (kv_n words).
+__global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs, int n2, uint32_t* kvbm,
+                                               int64_t kv_n) {
   __shared__ int wsum[4];
   const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * 256 + tid; i < kv_n; i += (int64_t)(gridDim.x - 1) * 256)
+      kvbm[i] = 0u;
+    return;
+  }
   const int B = seq.batch;
   int carry_q = 0, carry_k = 0;
   for (int base = 0; base < B; base += 256) {
@@ -136,19 +145,22 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
   const int nwords = (nbits + 31) >> 5;
   for (int w = lane; w < nwords; w += 64) {
     uint32_t v = 0;
-    if (sel.kind == SP_NONE) {
+    if (sel.kind == SP_NONE || kv_lists(sel.kind)) {
+      // the blocks [kb_lo, nbits) that hold allowed keys
       const int hi = nbits - w * 32;
       v = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
-      const int lb = kb_lo - w * 32;  // blocks below kb_lo hold no allowed key
+      const int lb = kb_lo - w * 32;
       if (lb >= 32)
         v = 0;
       else if (lb > 0)
         v &= ~((1u << lb) - 1u);
+      // per-KV-block lists: the blocks whose lists name this row's q-block
+      if (kv_lists(sel.kind)) v &= sel.kvbm[(int64_t)r * sel.kv_words + w];
     }
     bm[w] = v;
   }
   __syncthreads();
-  if (nbits > 0 && sel.kind != SP_NONE) {
+  if (nbits > 0 && sel.kind != SP_NONE && !kv_lists(sel.kind)) {
     if (sel.kind == SP_MASK || sel.kind == SP_SABI) {
       if (qb < sel.rows) {
         const int64_t row = (((int64_t)b * sel.hs + hs) * sel.rows + qb) * sel.width;
@@ -165,9 +177,11 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
           }
         }
       }
-    } else {  // SP_IDX over global q-blocks
-      if (qg < sel.rows) {
-        const int64_t rr = (int64_t)hs * sel.rows + qg;
+    } else {  // SP_IDX over global q-blocks, SP_IDX_B over local ones
+      const bool in_rows = sel.kind == SP_IDX ? qg < sel.rows : qb < sel.rows;
+      if (in_rows) {
+        const int64_t rr = sel.kind == SP_IDX ? (int64_t)hs * sel.rows + qg
+                                              : ((int64_t)b * sel.hs + hs) * sel.rows + qb;
         const int n = min(max(sel.count[rr], 0), sel.width);
         const int32_t* ix = reinterpret_cast<const int32_t*>(sel.sparse) + rr * sel.width;
         for (int t = lane; t < n; t += 64) {
@@ -179,6 +193,39 @@ __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, 
   }
   __syncthreads();
   return nbits;
+}
+
+// Per-KV-block lists (one wave per list): KV block kb of sequence b and
+// sparse head hs sets bit kb in the bitmap of row (hs, b, qb) for every
+// q-block qb among its list's first count entries that lies in [0, nQB_b).
+// Atomic ORs give the same bits in any order.
+__global__ __launch_bounds__(256) void k_kv_scatter(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t nlists) {
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int64_t L = (int64_t)blockIdx.x * 4 + wv;
+  if (L >= nlists) return;
+  const int TQB = ip.hdr[H_TQB], TKB = ip.hdr[H_TKB];
+  int b, hs, kb;
+  if (sel.kind == SP_KV) {  // [Hs, rows = totalKBlocks, W]
+    hs = (int)(L / sel.rows);
+    const int gk = (int)(L - (int64_t)hs * sel.rows);
+    if (gk >= TKB) return;
+    b = ip.kb_seq[gk];
+    kb = gk - ip.kbase[b];
+  } else {  // [B, Hs, rows, W]
+    kb = (int)(L % sel.rows);
+    const int64_t bh = L / sel.rows;
+    hs = (int)(bh % sel.hs);
+    b = (int)(bh / sel.hs);
+    if (kb >= cdiv(ip.skv[b], seq.by)) return;
+  }
+  const int nqb = cdiv(ip.sq[b], seq.bx);
+  const int n = min(max(sel.count[L], 0), sel.width);
+  const int32_t* lst = reinterpret_cast<const int32_t*>(sel.sparse) + L * sel.width;
+  const int64_t row0 = (int64_t)hs * TQB + ip.qbase[b];
+  for (int t = lane; t < n; t += 64) {
+    const int qb = lst[t];
+    if (qb >= 0 && qb < nqb) atomicOr(&sel.kvbm[(row0 + qb) * sel.kv_words + (kb >> 5)], 1u << (kb & 31));
+  }
 }
 
 // Also clears the column counters of the transpose (zero_n entries of col_cnt
@@ -537,7 +584,14 @@ hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd
                         int group, bool with_csc, hipStream_t st) {
   const bool merged = with_csc && radix_passes((int64_t)bd.cmax + 1) == 1 &&
                       radix_passes((int64_t)bd.kvkey_max + 1) == 1;
-  k_setup<<<1, 256, 0, st>>>(seq, ip, sel.hs, n2);
+  const bool kv = kv_lists(sel.kind);
+  const int64_t kv_n = kv ? bd.rbar * (int64_t)sel.kv_words : 0;
+  const unsigned clear_blocks = kv ? (unsigned)std::min<int64_t>(blocks_for(kv_n, 256), 1024) : 0;
+  k_setup<<<1 + clear_blocks, 256, 0, st>>>(seq, ip, sel.hs, n2, sel.kvbm, kv_n);
+  if (kv) {
+    const int64_t nlists = (int64_t)sel.hs * sel.rows * (sel.kind == SP_KV_B ? seq.batch : 1);
+    if (nlists > 0) k_kv_scatter<<<blocks_for(nlists, 4), 256, 0, st>>>(seq, sel, ip, nlists);
+  }
   const int words = (bd.nkb_max + 31) / 32 > 0 ? (bd.nkb_max + 31) / 32 : 1;
   const size_t lds = 4 * (size_t)words * 4;
   const unsigned rgrid = blocks_for(bd.rbar, 4);

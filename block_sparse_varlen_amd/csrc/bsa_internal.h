@@ -19,7 +19,8 @@ enum HeaderSlot {
   H_COUNT = 16  // header size in int32 (padded)
 };
 
-enum SparseKind { SP_NONE = 0, SP_MASK = 1, SP_SABI = 2, SP_IDX = 3 };
+enum SparseKind { SP_NONE = 0, SP_MASK = 1, SP_SABI = 2, SP_IDX = 3, SP_IDX_B = 4, SP_KV = 5, SP_KV_B = 6 };
+__host__ __device__ inline bool kv_lists(int kind) { return kind == SP_KV || kind == SP_KV_B; }
 
 // Attention work items are handed to the 8 XCDs in runs of XCD_SEG
 // consecutive items (xcd_item in bsa_attn.h); grids are padded to whole rounds.
@@ -43,7 +44,7 @@ struct Bounds {
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct Layout {
   size_t hdr, sq, skv, qbase, kbase, qb_seq, kb_seq;
-  size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work;
+  size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work, kvbm;
   size_t col_cnt, col_ptr, col_fill, qrows, kvkey0, kvval0, kvkey1, kvval1, kvhist, work_kv;
   size_t ndl, lse2;
   size_t index_end;  // bytes used by the index products
@@ -75,6 +76,10 @@ struct SelArgs {
   int32_t hs;      // Hs
   int32_t rows;    // selection tensor row dimension
   int32_t width;   // W
+  // per-KV-block lists: the rows' visited-block bitmaps the lists are first
+  // scattered into ([rows of the index][kv_words] words), else nullptr
+  uint32_t* kvbm;
+  int32_t kv_words;
 };
 
 struct IndexPtrs {

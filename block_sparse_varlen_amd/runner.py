@@ -13,14 +13,16 @@ import torch
 from . import (
     BSA_DTYPE_BF16, BSA_DTYPE_F16, BSA_DTYPE_FP8_E4M3, BSA_KV_PAGED, BSA_KV_TND, BSA_MASK_BAND, BSA_MASK_CAUSAL,
     BSA_MASK_NONE,
-    BSA_FLAG_INDEX_BUILT, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_IDX_I32, BSA_SPARSE_NONE, BSA_SPARSE_SABI_U16,
+    BSA_FLAG_INDEX_BUILT, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_IDX_BATCH_I32, BSA_SPARSE_IDX_I32,
+    BSA_SPARSE_KV_IDX_BATCH_I32, BSA_SPARSE_KV_IDX_I32, BSA_SPARSE_NONE, BSA_SPARSE_SABI_U16,
     bsa_build_index, bsa_bwd, bsa_fwd, bsa_get_workspace_size, bsa_index_view, problem,
 )
 
 _DTYPE = {"bf16": BSA_DTYPE_BF16, "f16": BSA_DTYPE_F16, "fp8": BSA_DTYPE_FP8_E4M3}
 _TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.uint8}
 _KIND = {"none": BSA_SPARSE_NONE, "mask": BSA_SPARSE_BLOCK_MASK, "sabi": BSA_SPARSE_SABI_U16,
-         "idx": BSA_SPARSE_IDX_I32}
+         "idx": BSA_SPARSE_IDX_I32, "idx_b": BSA_SPARSE_IDX_BATCH_I32, "kvidx": BSA_SPARSE_KV_IDX_I32,
+         "kvidx_b": BSA_SPARSE_KV_IDX_BATCH_I32}
 
 
 def problem_for(case):

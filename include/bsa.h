@@ -96,8 +96,25 @@ enum {
   /* int32 [Hs, sparse_rows, sparse_width] over global q-blocks (sparse_rows =
      totalQBlocks = sum_b ceil(Sq_b / block_x)), -1 = unused, plus
      `sparse_count` int32 [Hs, sparse_rows]: the first count entries are live
-     (GenericBlockSparseAttention page, sparseBlockIdx / sparseBlockCount) */
-  BSA_SPARSE_IDX_I32 = 3
+     (GenericBlockSparseAttention page, sparseBlockIdx / sparseBlockCount;
+     layoutSparsePattern 4, or 6 with Hs = N1) */
+  BSA_SPARSE_IDX_I32 = 3,
+  /* The same lists with a batch axis: int32 [B, Hs, sparse_rows, sparse_width]
+     over local q-blocks, count int32 [B, Hs, sparse_rows] (layoutSparsePattern
+     0, or 2 with Hs = N1) */
+  BSA_SPARSE_IDX_BATCH_I32 = 4,
+  /* Per-KV-block lists: int32 [Hs, sparse_rows, sparse_width], row gk =
+     kbase_b + kb over global KV blocks (sparse_rows = totalKBlocks = sum_b
+     ceil(Skv_b / block_y)) naming the local q-blocks that chose KV block kb,
+     -1 = unused, count int32 [Hs, sparse_rows] (layoutSparsePattern 5, or 7
+     with Hs = N1: "each KV block lists the Q blocks that chose it").  KV block
+     kb is selected for q-block qb when qb is among its list's first count
+     entries. */
+  BSA_SPARSE_KV_IDX_I32 = 5,
+  /* Per-KV-block lists with a batch axis: int32 [B, Hs, sparse_rows,
+     sparse_width] over local KV blocks, count int32 [B, Hs, sparse_rows]
+     (layoutSparsePattern 1, or 3 with Hs = N1) */
+  BSA_SPARSE_KV_IDX_BATCH_I32 = 6
 };
 
 /* Token masks.  BSA_MASK_BAND reads pre_tokens / next_tokens; either may be
@@ -141,7 +158,8 @@ typedef struct bsa_problem {
   int32_t sparse_kind;       /* BSA_SPARSE_* */
   int32_t sparse_heads;      /* Hs: N1 (pattern per q-head) or N2 (shared by a GQA group) */
   int32_t sparse_rows;       /* row dimension of the selection tensor (see BSA_SPARSE_*) */
-  int32_t sparse_width;      /* W: columns (mask), slots (sabi) or topK (idx, <= 256) */
+  int32_t sparse_width;      /* W: columns (mask), slots (sabi), topK (per-q-block lists, <= 256) or
+                                q-blocks per list (per-KV-block lists) */
   int32_t mask_type;         /* BSA_MASK_* */
   int32_t kv_layout;         /* BSA_KV_* */
   int32_t page_size;         /* paged: tokens per page, multiple of 64 */
@@ -170,7 +188,7 @@ bsa_status_t bsa_get_workspace_size(const bsa_problem_t* p, size_t* fwd_bytes, s
  *   cu_seqlens_kv int64 [B+1] (TND; NULL when paged)
  *   seqused_kv   int32 [B] (paged: required; TND: NULL)
  *   sparse       selection tensor per p->sparse_kind (NULL for NONE)
- *   sparse_count int32 [Hs, sparse_rows] (IDX only, else NULL)
+ *   sparse_count count tensor of the list kinds (IDX*, KV_IDX*), else NULL
  *   block_table  int32 [B, max_pages_per_seq] (paged only, else NULL); only
  *                entries for pages holding keys < Skv_b are read
  *   out          [T_q, N1, D] out_dtype (dtype when out_dtype is 0)

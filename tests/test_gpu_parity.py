@@ -113,6 +113,16 @@ def fwd_cases():
                                    density=0.9, band=(600, 0)),
         "none_band_bx1_by64": R(134, lens_q=[90, 40], lens_kv=[500, 200], N1=2, D=64, kind="none", bx=1, by=64,
                                 band=(70, 10)),
+        # the other layoutSparsePattern forms: batch-major per-q-block lists,
+        # per-KV-block lists (global and batch-major)
+        "idx_b_messy_gqa_causal": R(135, lens_q=[520, 300, 0], lens_kv=[600, 310, 90], N1=4, N2=2, D=128,
+                                    kind="idx_b", sparse_heads=2, messy=True, causal=True),
+        "kvidx_messy_perhead_paged": R(136, lens_q=[450, 333], lens_kv=[700, 260], N1=4, N2=2, D=128,
+                                       kind="kvidx", sparse_heads=4, messy=True, paged=True),
+        "kvidx_b_short_rows_band_f16": R(137, lens_q=[600, 420], lens_kv=[900, 400], N1=2, D=64, dtype="f16",
+                                         kind="kvidx_b", rows=5, band=(300, 60)),
+        "kvidx_bx64_by256_causal": R(138, lens_q=[700, 150], N1=2, D=128, kind="kvidx", bx=64, by=256,
+                                     causal=True),
     }
 
 
@@ -186,6 +196,13 @@ def bwd_cases():
                                    density=0.9, band=(600, 0)),
         "none_band_bx16_sq_gt_skv": R(233, lens_q=[300, 200], lens_kv=[180, 260], N1=2, D=128, kind="none", bx=16,
                                       band=(90, 20)),
+        # the other layoutSparsePattern forms
+        "idx_b_messy_gqa_causal": R(234, lens_q=[520, 300, 0], lens_kv=[600, 310, 90], N1=4, N2=2, D=128,
+                                    kind="idx_b", sparse_heads=2, messy=True, causal=True),
+        "kvidx_messy_perhead_paged": R(235, lens_q=[450, 333], lens_kv=[700, 260], N1=4, N2=2, D=128,
+                                       kind="kvidx", sparse_heads=4, messy=True, paged=True),
+        "kvidx_b_short_rows_band_f16": R(236, lens_q=[600, 420], lens_kv=[900, 400], N1=2, D=64, dtype="f16",
+                                         kind="kvidx_b", rows=5, band=(300, 60)),
     }
 
 
@@ -516,3 +533,50 @@ def test_bwd_config(n):
     ev = rel_fro(dv[ix], rv[ix])
     say(f"  config{n}: rel_fro dq={eq:.3e} dk={ek:.3e} dv={ev:.3e} (sampled)")
     assert eq <= tol and ek <= tol and ev <= tol
+
+
+# ------------------------------------------- per-KV-block lists at full size --
+
+def _kv_lists_of_mask(m):
+    """The mask case's selection as [Hs, totalKBlocks, W] per-KV-block lists
+    (each KV block names the q-blocks whose mask row selects it)."""
+    import copy
+    c = copy.copy(m)
+    lens_q = np.diff(m.cu_q)
+    lens_kv = np.diff(m.cu_kv)
+    nqb = [-(-int(x) // m.bx) for x in lens_q]
+    nkb = [-(-int(x) // m.by) for x in lens_kv]
+    Hs, W = m.sparse_heads, max(nqb)
+    idx = np.full((Hs, sum(nkb), W), -1, dtype=np.int32)
+    cnt = np.zeros((Hs, sum(nkb)), dtype=np.int32)
+    for b in range(m.B):
+        kb0 = sum(nkb[:b])
+        sel = m.sparse[b, :, :nqb[b], :nkb[b]] != 0  # [Hs, qb, kb]
+        for hs in range(Hs):
+            for kb in range(nkb[b]):
+                q = np.nonzero(sel[hs, :, kb])[0]
+                idx[hs, kb0 + kb, :len(q)] = q
+                cnt[hs, kb0 + kb] = len(q)
+    c.sparse_kind, c.sparse, c.count = "kvidx", idx, cnt
+    return c
+
+
+@pytest.mark.timeout(600)
+def test_kv_lists_long_context_equal_mask():
+    """The long-context workload's block mask given instead as per-KV-block
+    lists (layoutSparsePattern 7): the same index products and the same
+    forward and backward outputs, bit for bit."""
+    say("long-context workload as per-KV-block lists")
+    m = _cfg_bwd(5)
+    c = _kv_lists_of_mask(m)
+    dm, dc = DeviceCase(m, with_bwd=True), DeviceCase(c, with_bwd=True)
+    gm, gc = dm.index(True), dc.index(True)
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+        assert np.array_equal(gm[k], gc[k]), k
+    for d in (dm, dc):
+        d.fwd()
+        d.bwd()
+    torch.cuda.synchronize()
+    for nm in ("out", "lse", "dq", "dk", "dv"):
+        a, b = getattr(dm, nm), getattr(dc, nm)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), nm
