@@ -87,7 +87,7 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
   // valid descriptors without a compiled variant
   if (p->block_x > 4096) return BSA_ERR_INNER;
   if (p->dtype == BSA_DTYPE_FP8_E4M3 && p->head_dim != 128) return BSA_ERR_INNER;
-  if (p->block_y % 64 != 0 || p->block_y > 4096) return BSA_ERR_INNER;
+  if (p->block_y > 4096) return BSA_ERR_INNER;
   if (p->kv_layout == BSA_KV_PAGED && p->page_size % 64 != 0) return BSA_ERR_INNER;
   if ((int64_t)p->max_seqlen_kv > (int64_t)p->block_y * 65536 || (int64_t)p->max_seqlen_q > (int64_t)p->block_x * 65536)
     return BSA_ERR_INNER;
@@ -95,7 +95,6 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
 }
 
 bsa_status_t check_bwd_variant(const bsa_problem_t* p) {
-  if (p->block_y % 128 != 0) return BSA_ERR_INNER;
   if (p->dtype == BSA_DTYPE_FP8_E4M3) return BSA_ERR_INNER;  // forward-only quantisation
   return BSA_OK;
 }
@@ -560,7 +559,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.group = group;
   a.heads_per_row = p->sparse_heads == p->num_heads_q ? 1 : group;
   a.hs = p->sparse_heads;
-  a.sub_tiles = p->block_y / 128;
+  a.sub_tiles = (p->block_y + 127) / 128;
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
   if (p->total_kv > 0) {

@@ -229,38 +229,59 @@ __device__ __forceinline__ void settle_scalar_loads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The lane index computed on the spot (v_mbcnt), in an asm the compiler may
+// not hoist: inside a loop that runs at the register limit, a lane index kept
+// live across the loop gets spilled, and the wait for its reload would also
+// wait for the tile copies issued just before.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // One fp32 per row of a 64-row tile, loaded by one wave into LDS (lane l ->
 // bytes 4 l); rows at or past nvalid repeat row nvalid - 1.
 __device__ __forceinline__ void dma_rows_f32(float* lds, const float* g, int stride, int nvalid) {
-  const int r = min(lane_id(), nvalid - 1);
+  const int r = min(lane_id_here(), nvalid - 1);
   dma_to_lds<4>(g, 4u * (uint32_t)(r * stride), lds);
 }
 
-// Walk over the T-key sub-tiles of a CSR row: blocks cols[e0..e1), each cut
-// into by / T sub-tiles, keeping those whose first key is below `kend` (the
-// key bound of the item: Skv, or the causal limit of its last row + 1).  The
-// row's block list is held in a VGPR (lane l holds entry base + l), so
-// handing out a sub-tile is a lane read instead of a scalar memory round trip
-// on the critical path of the tile copies.  Rows of more than 64 entries
-// reload the register per 64 entries and wait for that load on the spot
-// (rare), which leaves the compiler no pending load of it to wait for
-// elsewhere -- such a wait would also drain the tile copies in flight.
+// Walk over the T-key sub-tiles of a CSR row: blocks cols[e0..e1), keeping
+// sub-tiles whose first key is below `kend` (the key bound of the item: Skv,
+// or its last row's window end + 1) and that end above `kstart` (its first
+// row's window start).  The row's block list is held in a VGPR (lane l holds
+// entry base + l), so handing out a sub-tile is a lane read instead of a
+// scalar memory round trip on the critical path of the tile copies.  Rows of
+// more than 64 entries reload the register per 64 entries and wait for that
+// load on the spot (rare), which leaves the compiler no pending load of it to
+// wait for elsewhere -- such a wait would also drain the tile copies in
+// flight.
+//
+// When block_y is a multiple of T each block is cut into block_y / T
+// sub-tiles.  Otherwise (block_y a multiple of 16) the walk hands out the
+// T-aligned windows of keys that meet a selected block, each window once,
+// with `gmask` naming its 16-key groups that lie in selected blocks (bit g:
+// keys 16 g .. 16 g + 15 of the window); the kernels mask the other groups.
+// Several small blocks then share one window's MFMAs, and a window never
+// crosses a T-aligned page boundary.
 template <int T = KT>
 struct RegTileWalk {
+  static constexpr uint32_t FULL = (1u << (T / 16)) - 1u;
   const int32_t* cols;
   int e, e1, base, s, nsub, by, kend;
+  bool grouped;
+  int wk;          // grouped: first key of the next window
+  uint32_t gmask;  // 16-key groups of the last sub-tile handed out that are selected
   int colv;
   // The caller waits for the initial load (any vmcnt wait covering it) before
-  // the first take<false>(); take<true>() reads its entry with a scalar load
+  // the first take<false>(); take<true>() reads its entries with scalar loads
   // instead, for a first sub-tile issued before that wait.
-  // kstart: the item's smallest allowed key (its first row's band start, 0
-  // without a band); sub-tiles that end below it are skipped.
   __device__ __forceinline__ void init(const int32_t* c, int e0, int e_end, int by_, int kend_, int kstart = 0) {
     cols = c;
     e1 = e_end;
     // the list is ascending: drop trailing blocks that start at or past kend
     // (only a slice of a q-block taller than 128 rows can end before the
-    // q-block's causal limit, so this loop rarely runs)
+    // q-block's window end, so this loop rarely runs)
     while (e1 > e0 && ldu(c, e1 - 1) * by_ >= kend_) --e1;
     // and leading blocks that end below kstart (band masks only)
     while (e0 < e1 && (ldu(c, e0) + 1) * by_ <= kstart) ++e0;
@@ -270,33 +291,63 @@ struct RegTileWalk {
     by = by_;
     nsub = by_ / T;
     kend = kend_;
-    // first sub-tile of the first block that reaches kstart
-    if (kstart > 0 && e0 < e1) s = max(0, (kstart - ldu(c, e0) * by_) / T);
+    grouped = by_ % T != 0;
+    gmask = FULL;
+    wk = 0;
+    if (e0 < e1) {
+      const int k0 = max(kstart, ldu(c, e0) * by_);
+      if (grouped) {
+        wk = k0 & ~(T - 1);
+        if (wk >= kend_) e = e1;
+      } else if (kstart > 0) {
+        s = (k0 - ldu(c, e0) * by_) / T;  // first sub-tile of the first block that reaches kstart
+      }
+    }
     colv = e0 + lane_id() < e_end ? c[e0 + lane_id()] : 0;
   }
   __device__ __forceinline__ bool valid() const { return e < e1; }
-  // first key of the current sub-tile; advances to the next one
-  template <bool SCALAR = false>
-  __device__ __forceinline__ int take() {
-    int c;
+  template <bool SCALAR>
+  __device__ __forceinline__ int entry(int ee) {
     if constexpr (SCALAR) {
-      c = ldu(cols, e);
+      return ldu(cols, ee);
     } else {
-      if (__builtin_expect(e - base >= 64, 0)) {
+      if (__builtin_expect(ee - base >= 64, 0)) {
         base += 64;
         colv = base + lane_id() < e1 ? cols[base + lane_id()] : 0;
         wait_vmcnt<0>();
         pin(colv);
       }
-      c = __builtin_amdgcn_readlane(colv, e - base);
+      return __builtin_amdgcn_readlane(colv, ee - base);
     }
-    const int key = c * by + s * T;
-    ++s;
-    if (s >= nsub || key + T >= kend) {
+  }
+  // first key of the current sub-tile (and its gmask); advances to the next one
+  template <bool SCALAR = false>
+  __device__ __forceinline__ int take() {
+    if (!grouped) {
+      const int key = entry<SCALAR>(e) * by + s * T;
+      ++s;
+      if (s >= nsub || key + T >= kend) {
+        ++e;
+        s = 0;
+      }
+      return key;
+    }
+    const int key0 = wk;
+    uint32_t m = 0;
+    while (e < e1) {  // the blocks that meet window [key0, key0 + T)
+      const int bs = entry<SCALAR>(e) * by, be = bs + by;
+      if (bs >= key0 + T) break;
+      const int glo = (max(bs, key0) - key0) >> 4, ghi = (min(be, key0 + T) - key0) >> 4;
+      m |= ((1u << ghi) - 1u) & ~((1u << glo) - 1u);
+      if (be > key0 + T) break;  // the block goes on in the next window
       ++e;
-      s = 0;
     }
-    return key;
+    gmask = m;
+    if (e < e1) {  // the next window: the next one, or the next block's first
+      wk = max(key0 + T, (entry<SCALAR>(e) * by) & ~(T - 1));
+      if (wk >= kend) e = e1;
+    }
+    return key0;
   }
 };
 

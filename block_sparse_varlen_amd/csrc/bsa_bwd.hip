@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 // The dP^T accumulator starts from -D (a loop-invariant register tile), and
 // key masks run only on sub-tiles that reach past Skv or outside a row's window.
 
-template <typename MF, int D, bool WIN, bool PAGED>
+template <typename MF, int D, int WMODE, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   using L = XorTile<D>;  // K: read row-major (S^T) and transposed (dQ^T); V: row-major (dP^T)
   constexpr int TILE = L::template bytes<KT>();
@@ -76,13 +76,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   // copies and the barriers
   const bool wave_active = wv * 32 < it.nrows;
   // with a token window (causal or band mask) key j is allowed for row i when
-  // i + qoff + win_lo <= j <= i + qoff + win_hi
+  // i + qoff + win_lo <= j <= i + qoff + win_hi; WMODE 1 has no lower end
+  // (causal, or a band with unbounded preTokens), WMODE 2 has both
+  constexpr bool WIN = WMODE != 0, LO = WMODE == 2;
   const int qoff = it.skv - it.sq;
   const int win_lo = a.seq.win_lo, win_hi = a.seq.win_hi;
   int kend = it.skv, kstart = 0;
   if (WIN) {
     kend = min(kend, it.row_lo + it.nrows - 1 + qoff + win_hi + 1);
-    kstart = max(0, it.row_lo + qoff + win_lo);
+    if (LO) kstart = max(0, it.row_lo + qoff + win_lo);
   }
 
   const int64_t qstride = (int64_t)a.n1 * D;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   for (int mt = 0; mt < NMT; ++mt) acc[mt] = zero16();
   const float c2 = a.sigma_log2e;
   const int lim = WIN ? min(it.skv - 1, my_row + qoff + win_hi) : it.skv - 1;
-  const int lo = WIN ? my_row + qoff + win_lo : 0;
+  const int lo = LO ? my_row + qoff + win_lo : 0;
 
   Dma dma;
   dma.init(a.n2 * D);
@@ -123,11 +125,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   KvAddr<PAGED> kva;
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   int key_next = 0;
+  uint32_t gm_next = 0xFu;  // selected 16-key groups of that sub-tile
   // the first sub-tile goes out before the block list register has landed
   auto issue = [&](int stage, auto first) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.template take<decltype(first)::value>();
     key_next = key0;
+    gm_next = ld.gmask;
     const int64_t off = kva.off(key0);
     dma.issue(st, kp + off, it.skv - key0);
     dma.issue(st + TILE, vp + off, it.skv - key0);
@@ -137,6 +141,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   int stage = 0;
   while (more) {
     const int key0 = key_next;     // the sub-tile computed in this step
+    const uint32_t gm = gm_next;   // its 16-key groups in selected blocks
     wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
     more = ld.valid();
@@ -148,7 +153,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
     const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
-    const bool edge = key0 + KT > it.skv || (WIN && (key0 + KT - 1 > rw0 + win_hi || key0 < rw0 + 31 + win_lo));
+    const bool edge = key0 + KT > it.skv || gm != 0xFu ||
+                      (WIN && key0 + KT - 1 > rw0 + win_hi) || (LO && key0 < rw0 + 31 + win_lo);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // 32-key halves of the sub-tile
       f32x16_t s = zero16(), dp = ndt;
@@ -166,7 +172,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (key > lim || key < lo) s[i] = 0.f;
+          if (key > lim || (LO && key < lo)) s[i] = 0.f;
+        }
+        if (gm != 0xFu) {  // 16-key groups outside the selected blocks (block_y not a multiple of 64)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (!((gm >> (2 * t + (i >> 3))) & 1u)) s[i] = 0.f;
         }
       }
 #pragma unroll
@@ -263,12 +274,13 @@ struct DkdvShape {
 constexpr int DKDV_KEYS = 128;  // keys per work item
 constexpr int DKDV_STAGES = 2;  // LDS ring depth (two workgroups per CU share the LDS)
 
-template <typename MF, int D, bool WIN, bool PAGED>
+template <typename MF, int D, int WMODE, bool PAGED>
 __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 1) void k_bwd_dkdv(BwdArgs a) {
   constexpr int NT = DkdvShape<D>::NT;
   constexpr int NW = DkdvShape<D>::NW;
   constexpr int LOOK = DkdvShape<D>::LOOK;  // MFMA operands read this many steps ahead
   static_assert(32 * NT * NW == DKDV_KEYS, "a workgroup covers the 128-key tile");
+  constexpr bool WIN = WMODE != 0, LO = WMODE == 2;  // token window; LO: with a lower end
   using QL = XorTile<D>;  // Q and dO: read row-major (S, dP) and transposed (dK^T, dV^T)
   constexpr int TILE = QL::template bytes<QS>();
   constexpr int STAGE = 2 * TILE + 2 * QS * 4;  // Q, dO, lse, D
@@ -300,7 +312,12 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
     skv = (int)(ldu(a.seq.cu_kv, b + 1) - kv0);
   }
   const int key_lo = kb * a.seq.by + sub * DKDV_KEYS;
-  if (key_lo >= skv) return;
+  // keys of this item: the tile's part of block kb below Skv.  A block_y
+  // that is not a multiple of 128 leaves the block's last tile partial: its
+  // other keys (the next block's) are computed -- dK / dV columns do not mix
+  // -- but never stored.
+  const int kcap = min(skv, (kb + 1) * a.seq.by);
+  if (key_lo >= kcap) return;
   const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // this lane's keys: column lane % 32 of the wave's 32-key tiles
   const int key_w = key_lo + 32 * NT * wv + (lane & 31);
@@ -353,8 +370,8 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
   ld.sq = sq;
   ld.qoff = qoff;
   ld.key_min = key_lo;
-  ld.key_max = min(key_lo + DKDV_KEYS, skv) - 1;
-  ld.win = WIN;
+  ld.key_max = min(key_lo + DKDV_KEYS, kcap) - 1;
+  ld.win = WIN;  // (win_lo is -WIN_INF without a lower end, so ok() needs no mode)
   ld.win_lo = a.seq.win_lo;
   ld.win_hi = a.seq.win_hi;
   ld.bx = a.seq.bx;
@@ -404,8 +421,8 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 
     // Rows past the q-block or sequence end, or keys outside some row's
     // window, need masks; every other tile takes the mask-free path.
-    const bool masked = nrows < QS || (WIN && (key_lo + DKDV_KEYS - 1 > r0 + qoff + win_hi ||
-                                               key_lo < r0 + QS - 1 + qoff + win_lo));
+    const bool masked = nrows < QS || (WIN && key_lo + DKDV_KEYS - 1 > r0 + qoff + win_hi) ||
+                        (LO && key_lo < r0 + QS - 1 + qoff + win_lo);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
       // dP starts from -D of each element's row, so the MFMAs leave dP - D
@@ -459,7 +476,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             const int kd = key_w + 32 * n - (r0 + rl + qoff);  // key minus the row's diagonal key
-            if ((WIN && (kd > win_hi || kd < win_lo)) || rl >= nrows) {
+            if ((WIN && kd > win_hi) || (LO && kd < win_lo) || rl >= nrows) {
               s[n][i] = 0.f;
               dp[n][i] = 0.f;
             }
@@ -499,7 +516,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int key = key_w + 32 * n;
-    if (key < skv) {
+    if (key < kcap) {
       const int64_t orow = key_row(key);
       uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + orow;
       uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + orow;
@@ -514,10 +531,11 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 
 template <typename MF, int D, bool PAGED>
 hipError_t launch_dq_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.seq.masked)
-    k_bwd_dq<MF, D, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
-  else
-    k_bwd_dq<MF, D, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
+  switch (window_mode(a.seq)) {
+    case 0: k_bwd_dq<MF, D, 0, PAGED><<<(unsigned)grid, 256, 0, st>>>(a); break;
+    case 1: k_bwd_dq<MF, D, 1, PAGED><<<(unsigned)grid, 256, 0, st>>>(a); break;
+    default: k_bwd_dq<MF, D, 2, PAGED><<<(unsigned)grid, 256, 0, st>>>(a); break;
+  }
   return hipGetLastError();
 }
 template <typename MF, int D>
@@ -527,10 +545,11 @@ hipError_t launch_dq_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
 template <typename MF, int D, bool PAGED>
 hipError_t launch_dkdv_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
   constexpr unsigned threads = 64 * DkdvShape<D>::NW;
-  if (a.seq.masked)
-    k_bwd_dkdv<MF, D, true, PAGED><<<(unsigned)grid, threads, 0, st>>>(a);
-  else
-    k_bwd_dkdv<MF, D, false, PAGED><<<(unsigned)grid, threads, 0, st>>>(a);
+  switch (window_mode(a.seq)) {
+    case 0: k_bwd_dkdv<MF, D, 0, PAGED><<<(unsigned)grid, threads, 0, st>>>(a); break;
+    case 1: k_bwd_dkdv<MF, D, 1, PAGED><<<(unsigned)grid, threads, 0, st>>>(a); break;
+    default: k_bwd_dkdv<MF, D, 2, PAGED><<<(unsigned)grid, threads, 0, st>>>(a); break;
+  }
   return hipGetLastError();
 }
 template <typename MF, int D>

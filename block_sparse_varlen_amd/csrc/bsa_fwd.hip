@@ -35,7 +35,7 @@ namespace {
 // lse; only the rounding differs.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <typename MF, int D, bool WIN, bool PAGED>
+template <typename MF, int D, int WMODE, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   // K is read row-major only (XOR-permuted chunks), V transposed only (rows
   // padded by 64 bytes): both layouts keep their read pattern conflict free
@@ -60,13 +60,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   // sequence end) only helps with the copies and the barriers
   const bool wave_active = wv * 32 < it.nrows;
   // with a token window (causal or band mask) key j is allowed for row i when
-  // i + qoff + win_lo <= j <= i + qoff + win_hi
+  // i + qoff + win_lo <= j <= i + qoff + win_hi; WMODE 1 has no lower end
+  // (causal, or a band with unbounded preTokens), WMODE 2 has both
+  constexpr bool WIN = WMODE != 0, LO = WMODE == 2;
   const int qoff = it.skv - it.sq;
   const int win_lo = a.seq.win_lo, win_hi = a.seq.win_hi;
   int kend = it.skv, kstart = 0;
   if (WIN) {
     kend = min(kend, it.row_lo + it.nrows - 1 + qoff + win_hi + 1);
-    kstart = max(0, it.row_lo + qoff + win_lo);
+    if (LO) kstart = max(0, it.row_lo + qoff + win_lo);
   }
 
   // Q^T operand (B of S^T = K Q^T): lane holds row my_row, d = 16 kk + 8 (lane / 32) .. + 7
@@ -103,11 +105,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   KvAddr<PAGED> kva;
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   int key_next = 0;
+  uint32_t gm_next = 0xFu;  // selected 16-key groups of that sub-tile
   // the first sub-tile goes out before the block list register has landed
   auto issue = [&](int stage, auto first) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.template take<decltype(first)::value>();
     key_next = key0;
+    gm_next = ld.gmask;
     const int64_t off = kva.off(key0);
     kdma.issue(st, kbase_p + off, it.skv - key0);
     vdma.issue(st + KTILE, vbase_p + off, it.skv - key0);
@@ -117,6 +121,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   int stage = 0;
   while (more) {
     const int key0 = key_next;     // the sub-tile computed in this step
+    const uint32_t gm = gm_next;   // its 16-key groups in selected blocks
     wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
     more = ld.valid();
@@ -138,17 +143,25 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
                               [&](int i, const u32x4_t& op) { s[i & 1] = MF::mfma(op, qf[i >> 1], s[i & 1]); });
     // ---- masks: keys past Skv, outside the rows' windows (edge sub-tiles only) ----
     const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
-    const bool edge = key0 + KT > it.skv || (WIN && (key0 + KT - 1 > rw0 + win_hi || key0 < rw0 + 31 + win_lo));
+    const bool edge = key0 + KT > it.skv || gm != 0xFu ||
+                      (WIN && key0 + KT - 1 > rw0 + win_hi) || (LO && key0 < rw0 + 31 + win_lo);
     if (edge) {
       const int lim = WIN ? min(it.skv - 1, my_row + qoff + win_hi) : it.skv - 1;
-      const int lo = WIN ? my_row + qoff + win_lo : 0;
+      const int lo = LO ? my_row + qoff + win_lo : 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (key > lim || key < lo) s[t][i] = -INFINITY;
+          if (key > lim || (LO && key < lo)) s[t][i] = -INFINITY;
         }
+      if (gm != 0xFu) {  // 16-key groups outside the selected blocks (block_y not a multiple of 64)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (!((gm >> (2 * t + (i >> 3))) & 1u)) s[t][i] = -INFINITY;
+      }
     }
     // ---- online softmax (row = this lane's column) ----
     const float mx = half_max(max32(s[0], s[1]));
@@ -206,10 +219,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 
 template <typename MF, int D, bool PAGED>
 hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.seq.masked)
-    k_fwd<MF, D, true, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
-  else
-    k_fwd<MF, D, false, PAGED><<<(unsigned)grid, 256, 0, st>>>(a);
+  switch (window_mode(a.seq)) {
+    case 0: k_fwd<MF, D, 0, PAGED><<<(unsigned)grid, 256, 0, st>>>(a); break;
+    case 1: k_fwd<MF, D, 1, PAGED><<<(unsigned)grid, 256, 0, st>>>(a); break;
+    default: k_fwd<MF, D, 2, PAGED><<<(unsigned)grid, 256, 0, st>>>(a); break;
+  }
   return hipGetLastError();
 }
 

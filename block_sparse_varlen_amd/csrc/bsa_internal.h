@@ -68,6 +68,9 @@ struct SeqArgs {
 // Any window edge at or beyond this many tokens acts as unbounded (sequence
 // lengths stay below 2^28, so i + (Skv - Sq) + win never overflows int32).
 constexpr int32_t WIN_INF = 1 << 30;
+// Kernel variant of the token window: 0 none, 1 an upper end only (causal, or
+// a band with unbounded preTokens), 2 both ends.
+inline int window_mode(const SeqArgs& s) { return !s.masked ? 0 : s.win_lo <= -WIN_INF ? 1 : 2; }
 
 struct SelArgs {
   const void* sparse;
@@ -161,7 +164,7 @@ struct BwdArgs {
   int32_t page_size, max_pages;
   int64_t page_stride;     // elements
   int32_t n1, n2, group, heads_per_row, hs;
-  int32_t sub_tiles;       // block_y / 128 (dK/dV tiles per KV block)
+  int32_t sub_tiles;       // ceil(block_y / 128): dK/dV tiles per KV block (the last one may be partial)
   float sigma;
   float sigma_log2e;
 };

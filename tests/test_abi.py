@@ -97,7 +97,7 @@ def test_workspace_size_ok():
     (dict(block_x=64), bsa.BSA_OK),         # half-height work items
     (dict(block_x=192), bsa.BSA_OK),        # a 128-row and a 64-row work item per q-block
     (dict(block_x=4097), bsa.BSA_ERR_INNER),  # valid, no compiled variant
-    (dict(block_y=48), bsa.BSA_ERR_INNER),
+    (dict(block_y=4096 + 16), bsa.BSA_ERR_INNER),
     (dict(dtype=bsa.BSA_DTYPE_FP8_E4M3), bsa.BSA_ERR_PARAM_INVALID),  # e4m3 needs an fp16 / bf16 out_dtype
     (dict(dtype=bsa.BSA_DTYPE_BF16, out_dtype=bsa.BSA_DTYPE_F16), bsa.BSA_ERR_PARAM_INVALID),
 ])
@@ -118,8 +118,9 @@ def test_paged_backward_sizes():
     p64 = good(kv_layout=bsa.BSA_KV_PAGED, page_size=64, max_pages_per_seq=8, page_stride=64 * 2 * 128,
                total_kv=10)
     assert status(p64, fwd=False, bwd=True) == bsa.BSA_OK
-    # the backward's KV tiles are 128 keys: block_y = 64 has no backward variant
-    assert status(good(block_y=64), fwd=False, bwd=True) == bsa.BSA_ERR_INNER
+    # any multiple of 16 has both passes (the last 128-key dK/dV tile of a block may be partial)
+    for by in (16, 48, 64, 80, 192):
+        assert status(good(block_y=by), fwd=True, bwd=True) == bsa.BSA_OK
 
 
 def _fwd_status(p, ws_bytes=1 << 30, **ptrs):

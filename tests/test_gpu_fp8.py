@@ -39,6 +39,9 @@ def cases():
         # band mask with Sq != Skv
         "sabi_band_f16": R(409, lens_q=[450, 200], lens_kv=[520, 330], N1=2, kind="sabi", band=(150, 30),
                            dense_q=True, out_dtype="f16", **F),
+        # 48-key blocks: 64-key windows with masked groups
+        "mask_by48_paged": R(410, lens_q=[300, 200], lens_kv=[333, 450], N1=4, N2=2, kind="mask", by=48,
+                             paged=True, out_dtype="bf16", **F),
     }
 
 

@@ -123,6 +123,16 @@ def fwd_cases():
                                          kind="kvidx_b", rows=5, band=(300, 60)),
         "kvidx_bx64_by256_causal": R(138, lens_q=[700, 150], N1=2, D=128, kind="kvidx", bx=64, by=256,
                                      causal=True),
+        # block_y a multiple of 16: 64-key windows shared by several small
+        # blocks, with the unselected 16-key groups masked
+        "mask_by16_causal": R(139, lens_q=[300, 170], lens_kv=[330, 170], N1=2, D=128, kind="mask", by=16,
+                              causal=True, density=0.4),
+        "sabi_by48_gqa_f16": R(140, lens_q=[400, 260], N1=4, N2=2, D=64, dtype="f16", kind="sabi",
+                               sparse_heads=2, by=48),
+        "idx_by80_paged_causal": R(141, lens_q=[520, 300], lens_kv=[700, 310], N1=4, N2=2, D=128, kind="idx",
+                                   sparse_heads=2, by=80, paged=True, causal=True, messy=True),
+        "none_by16_band": R(142, lens_q=[260, 100], N1=2, D=64, kind="none", by=16, band=(100, 17)),
+        "kvidx_by32_bx32": R(143, lens_q=[350, 123], lens_kv=[400, 150], N1=2, D=128, kind="kvidx", bx=32, by=32),
     }
 
 
@@ -203,6 +213,15 @@ def bwd_cases():
                                        kind="kvidx", sparse_heads=4, messy=True, paged=True),
         "kvidx_b_short_rows_band_f16": R(236, lens_q=[600, 420], lens_kv=[900, 400], N1=2, D=64, dtype="f16",
                                          kind="kvidx_b", rows=5, band=(300, 60)),
+        # block_y not a multiple of 128: a KV block's last 128-key dK/dV tile
+        # is partial (64, 16, 48, 80 keys)
+        "mask_by64": R(237, lens_q=[300, 170], lens_kv=[330, 200], N1=2, D=128, kind="mask", by=64),
+        "mask_by16_causal": R(238, lens_q=[300, 170], N1=2, D=64, kind="mask", by=16, causal=True, density=0.4),
+        "sabi_by48_gqa_paged_f16": R(239, lens_q=[400, 260], N1=4, N2=2, D=128, dtype="f16", kind="sabi",
+                                     sparse_heads=2, by=48, paged=True),
+        "idx_by80_band": R(240, lens_q=[520, 300], lens_kv=[700, 310], N1=4, N2=2, D=128, kind="idx",
+                           sparse_heads=4, by=80, band=(200, 30)),
+        "sabi_by192_causal": R(241, lens_q=[700, 400], N1=2, D=128, kind="sabi", by=192, causal=True),
     }
 
 
@@ -297,16 +316,12 @@ def nan_fill(*ts):
 def test_index_bit_exact(name):
     case = FWD[name]
     say(f"index {name}")
-    with_csc = case.by % 128 == 0  # backward variants need 128-key tiles
-    dc = DeviceCase(case, with_bwd=with_csc)
-    got = dc.index(with_csc)
-    ref = oracle.index_products(case, with_csc=with_csc)
+    dc = DeviceCase(case, with_bwd=True)
+    got = dc.index(True)
+    ref = oracle.index_products(case, with_csc=True)
     assert got["R"] == ref["R"]
-    for k in ("row_ptr", "cols", "work"):
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
         assert np.array_equal(got[k], ref[k]), k
-    if with_csc:
-        for k in ("col_ptr", "qrows", "work_kv"):
-            assert np.array_equal(got[k], ref[k]), k
 
 
 # --------------------------------------------------------------------- fwd --
