@@ -154,7 +154,7 @@ typedef struct bsa_problem {
   int32_t max_seqlen_kv;     /* upper bound on every Skv_b */
   int32_t block_x;           /* q rows per selection block; 1 .. 4096 (work items hold up to 128 rows of one
                                 q-block, so block_x below 128 leaves part of each item idle) */
-  int32_t block_y;           /* keys per selection block; multiple of 64 (of 128 for bsa_bwd), <= 4096 */
+  int32_t block_y;           /* keys per selection block; multiple of 16, <= 4096 */
   int32_t sparse_kind;       /* BSA_SPARSE_* */
   int32_t sparse_heads;      /* Hs: N1 (pattern per q-head) or N2 (shared by a GQA group) */
   int32_t sparse_rows;       /* row dimension of the selection tensor (see BSA_SPARSE_*) */
@@ -226,9 +226,9 @@ bsa_status_t bsa_fwd_noalloc(const bsa_problem_t* p, const void* q, const void* 
  * shape.  In the paged layout dk / dv are written at the (page, slot) of every
  * key below seqused_kv[b] of every sequence (zeros for keys no row attends)
  * and the rest of the page pool is left as it was; two sequences must not
- * share a page (their gradients would be written, not summed).  Needs
- * block_y a multiple of 128 (else BSA_ERR_INNER).  dQ is computed by a
- * separate Q-block-major pass, so results are deterministic run to run. */
+ * share a page (their gradients would be written, not summed).  dQ is
+ * computed by a separate Q-block-major pass, so results are deterministic
+ * run to run. */
 bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse,
                      const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
