@@ -34,7 +34,7 @@ BSA_SPARSE_NONE, BSA_SPARSE_BLOCK_MASK, BSA_SPARSE_SABI_U16, BSA_SPARSE_IDX_I32 
 BSA_SPARSE_IDX_BATCH_I32, BSA_SPARSE_KV_IDX_I32, BSA_SPARSE_KV_IDX_BATCH_I32 = 4, 5, 6
 BSA_MASK_NONE, BSA_MASK_CAUSAL, BSA_MASK_BAND = 0, 1, 2
 BSA_KV_TND, BSA_KV_PAGED = 0, 1
-BSA_FLAG_INDEX_BUILT = 1
+BSA_FLAG_INDEX_BUILT, BSA_FLAG_DETERMINISTIC, BSA_FLAG_DQ_ATOMIC = 1, 2, 4
 (BSA_KERNEL_INDEX, BSA_KERNEL_FWD, BSA_KERNEL_BWD_PRE, BSA_KERNEL_BWD_DKDV, BSA_KERNEL_BWD_DQ) = range(5)
 KERNEL_NAMES = {0: "index", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq"}
 

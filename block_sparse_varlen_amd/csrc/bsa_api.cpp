@@ -83,7 +83,9 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
     if (p->page_stride < (int64_t)p->page_size * row || p->page_stride % row != 0) return BSA_ERR_PARAM_INVALID;
   }
   if (!(p->scale >= 0.0) || !std::isfinite(p->scale)) return BSA_ERR_PARAM_INVALID;
-  if ((p->flags & ~(uint32_t)BSA_FLAG_INDEX_BUILT) != 0) return BSA_ERR_PARAM_INVALID;
+  if ((p->flags & ~(uint32_t)(BSA_FLAG_INDEX_BUILT | BSA_FLAG_DETERMINISTIC | BSA_FLAG_DQ_ATOMIC)) != 0)
+    return BSA_ERR_PARAM_INVALID;
+  if ((p->flags & BSA_FLAG_DETERMINISTIC) && (p->flags & BSA_FLAG_DQ_ATOMIC)) return BSA_ERR_PARAM_INVALID;
   // valid descriptors without a compiled variant
   if (p->block_x > 4096) return BSA_ERR_INNER;
   if (p->dtype == BSA_DTYPE_FP8_E4M3 && p->head_dim != 128) return BSA_ERR_INNER;
@@ -123,6 +125,9 @@ Bounds make_bounds(const bsa_problem_t* p) {
   b.kvkey_max = (p->sparse_heads == p->num_heads_q ? group : 1) * std::max<int32_t>(b.nqb_max, 1);
   return b;
 }
+
+// dQ by fp32 atomics inside the dK/dV kernel (else the separate pass)
+bool dq_atomic(const bsa_problem_t* p) { return (p->flags & BSA_FLAG_DQ_ATOMIC) != 0; }
 
 // 32-bit words of one row's visited-block bitmap
 int64_t kv_words(const Bounds& b) { return std::max<int64_t>((b.nkb_max + 31) / 32, 1); }
@@ -175,6 +180,7 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   if (with_dl) {
     L.ndl = take((size_t)p->total_q * p->num_heads_q * 4);
     L.lse2 = take((size_t)p->total_q * p->num_heads_q * 4);
+    if (dq_atomic(p)) L.dq_acc = take((size_t)p->total_q * p->num_heads_q * p->head_dim * 4);
   }
   L.total = off;
   return L;
@@ -521,7 +527,10 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
 
   float* ndl = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ndl);
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse2);
-  BwdPreArgs pa{out, dout, lse, ndl, lse2, p->total_q * p->num_heads_q};
+  float* acc = dq_atomic(p) ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.dq_acc) : nullptr;
+  // (the atomic dQ accumulator is cleared by k_bwd_pre, a kernel rather than
+  // a memset, so the call can be captured in a HIP graph)
+  BwdPreArgs pa{out, dout, lse, ndl, lse2, acc, p->total_q * p->num_heads_q};
   prof_begin(BSA_KERNEL_BWD_PRE, s);
   e = launch_bwd_pre(pa, p->dtype, p->head_dim, s);
   prof_end(BSA_KERNEL_BWD_PRE, s);
@@ -538,6 +547,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.dq_acc = acc;
   a.seq = seq;
   a.hdr = ip.hdr;
   a.qb_seq = ip.qb_seq;
@@ -570,7 +580,10 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   }
   if (p->total_q > 0) {
     prof_begin(BSA_KERNEL_BWD_DQ, s);
-    e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128)), s);
+    if (acc)
+      e = launch_dq_convert(acc, dq, p->total_q * p->num_heads_q * p->head_dim, a.sigma, p->dtype, s);
+    else
+      e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128)), s);
     prof_end(BSA_KERNEL_BWD_DQ, s);
   }
   return from_hip(e);

@@ -10,9 +10,12 @@
 //
 // dK/dV are owner-computed: one workgroup per 128-key tile of one KV head,
 // looping over the q-heads of its GQA group and the q-blocks that selected
-// the tile (the transposed, per-KV-block index lists).  dQ is a separate
-// Q-block-major pass over the forward's per-q-block lists, so no output is
-// accumulated with atomics and results are deterministic run to run.
+// the tile (the transposed, per-KV-block index lists).  dQ comes either from
+// a separate Q-block-major pass over the forward's per-q-block lists (no
+// atomics, deterministic run to run), or from the dK/dV kernel itself, which
+// adds each stage's dS K into an fp32 accumulator with atomics that a last
+// kernel scales and converts (the order of the additions, and so the last
+// bits, vary from run to run).
 #include <type_traits>
 
 #include "bsa_attn.h"
@@ -45,6 +48,26 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     a.ndl[row] = -acc;
     a.lse2[row] = a.lse[row] * LOG2E;
   }
+  if (a.dq_acc && row < a.rows) {  // clear this chunk of the atomic dQ accumulator
+    float4* z = reinterpret_cast<float4*>(a.dq_acc + row * D + c * 8);
+    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// dq = scale * acc, 8 elements per thread
+template <typename MF>
+__global__ __launch_bounds__(256) void k_dq_convert(const float* acc, uint16_t* dq, int64_t n8, float sigma) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float4 x = reinterpret_cast<const float4*>(acc)[2 * i];
+  const float4 y = reinterpret_cast<const float4*>(acc)[2 * i + 1];
+  u32x4_t r;
+  r.x = MF::pack(x.x * sigma, x.y * sigma);
+  r.y = MF::pack(x.z * sigma, x.w * sigma);
+  r.z = MF::pack(y.x * sigma, y.y * sigma);
+  r.w = MF::pack(y.z * sigma, y.w * sigma);
+  reinterpret_cast<u32x4_t*>(dq)[i] = r;
 }
 
 // -------------------------------------------------------------------- dQ --
@@ -261,24 +284,37 @@ struct ColWalk {
   __device__ __forceinline__ int row_end() const { return min((ldu(qrows, e) + 1) * bx, sq); }
 };
 
+constexpr int DKDV_KEYS = 128;  // keys per work item
+constexpr int DKDV_STAGES = 2;  // LDS ring depth
+
 // Workgroup shape of the dK/dV kernel: NW waves of NT 32-key tiles.  Two
 // waves of 64 keys, two workgroups per CU (one wave per SIMD): each Q / dO
 // operand read from LDS feeds two MFMAs.  Four waves of 32 keys (two waves
 // per SIMD, so one wave's softmax could hide behind the other's MFMAs) need
 // ~280 registers at D = 128 against the 256 a wave then gets; the spilled
 // build was 22 % slower, so both head dims use the 64-key waves.
-template <int D>
+//
+// With atomic dQ (DQA) the kernel also forms dQ += dS K per stage, which
+// needs dS with the query rows on the lanes and K with the features on the
+// lanes -- both transposed from what the dK/dV products hold -- so K and
+// each half's dS go through LDS (32 + 2 x 12 KiB), and one workgroup of four
+// 32-key waves takes a CU.
+template <int D, bool DQA>
 struct DkdvShape {
-  static constexpr int NT = 2, NW = 2, LOOK = 4;
+  static constexpr int NT = DQA ? 1 : 2, NW = DQA ? 4 : 2, LOOK = 4;
+  static_assert(!DQA || D / 32 <= NW, "atomic dQ: one feature tile per wave");
 };
-constexpr int DKDV_KEYS = 128;  // keys per work item
-constexpr int DKDV_STAGES = 2;  // LDS ring depth (two workgroups per CU share the LDS)
+// dS tile of the atomic dQ: rows = the item's 128 keys, columns = a half's
+// 32 query rows, rows padded by 32 bytes (transposed reads of 4 rows x 32
+// bytes land on distinct banks)
+using DsTile = PadTile<32, 32>;
+constexpr int DS_BYTES = DsTile::bytes<DKDV_KEYS>();
 
-template <typename MF, int D, int WMODE, bool PAGED>
-__global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 1) void k_bwd_dkdv(BwdArgs a) {
-  constexpr int NT = DkdvShape<D>::NT;
-  constexpr int NW = DkdvShape<D>::NW;
-  constexpr int LOOK = DkdvShape<D>::LOOK;  // MFMA operands read this many steps ahead
+template <typename MF, int D, int WMODE, bool PAGED, bool DQA>
+__global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(BwdArgs a) {
+  constexpr int NT = DkdvShape<D, DQA>::NT;
+  constexpr int NW = DkdvShape<D, DQA>::NW;
+  constexpr int LOOK = DkdvShape<D, DQA>::LOOK;  // MFMA operands read this many steps ahead
   static_assert(32 * NT * NW == DKDV_KEYS, "a workgroup covers the 128-key tile");
   constexpr bool WIN = WMODE != 0, LO = WMODE == 2;  // token window; LO: with a lower end
   using QL = XorTile<D>;  // Q and dO: read row-major (S, dP) and transposed (dK^T, dV^T)
@@ -287,7 +323,8 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
   constexpr int NMT = D / 32;
   constexpr int NKK = D / 16;
   using Dma = DmaXor<D, QS, NW>;
-  __shared__ __attribute__((aligned(16))) char smem[DKDV_STAGES * STAGE];
+  constexpr int KT_BYTES = DQA ? QL::template bytes<DKDV_KEYS>() : 0;  // atomic dQ: K of the item
+  __shared__ __attribute__((aligned(16))) char smem[DKDV_STAGES * STAGE + (DQA ? KT_BYTES + 2 * DS_BYTES : 0)];
 
   const int KVI = ldu(a.hdr, H_KVITEMS);
   const int64_t flat = xcd_item(blockIdx.x);
@@ -344,6 +381,16 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
       vf[n][kk] = key < skv ? gload16(reinterpret_cast<const uint16_t*>(a.v) + krow + 16 * kk) : zero_u4();
     }
   }
+  char* const kt = smem + DKDV_STAGES * STAGE;  // atomic dQ: K rows of the item's keys
+  char* const dsbuf = kt + KT_BYTES;             // atomic dQ: two dS tiles
+  Operands<DsTile, 32> dsof;
+  if constexpr (DQA) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      lds_write16(kt, QL::chunk_off(32 * NT * wv + (lane & 31), 2 * kk + (lane >> 5)), kf[0][kk]);
+    dsof.init();
+    __syncthreads();
+  }
   f32x16_t dk[NT][NMT], dv[NT][NMT];
 #pragma unroll
   for (int n = 0; n < NT; ++n)
@@ -380,7 +427,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
   ld.half = 0;
   ld.open(0);
   ld.settle();
-  int r0_next = 0, rend_next = 0;
+  int r0_next = 0, rend_next = 0, hh_next = 0;
 
   Dma dma;
   dma.init(qstride);
@@ -392,6 +439,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
     const int r0 = ld.row0();
     r0_next = r0;
     rend_next = ld.row_end();
+    hh_next = ld.hh;
     const int nvalid = sq - r0;
     const int64_t off = (q0 + r0) * (int64_t)qstride + (int64_t)h * D;
     dma.issue(st, qp + off, nvalid);
@@ -408,6 +456,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
   while (more) {
     const int r0 = r0_next;            // the tile computed in this step
     const int nrows = rend_next - r0;  // its rows inside the q-block and the sequence (may exceed QS)
+    const int hh_cur = hh_next;        // its q-head within the group
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // every wave's loads landed; the other stage is no longer read
     more = ld.valid();
@@ -421,8 +470,10 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 
     // Rows past the q-block or sequence end, or keys outside some row's
     // window, need masks; every other tile takes the mask-free path.
+    // (atomic dQ also masks the keys of a partial tile past the block end:
+    // their dS would reach dQ)
     const bool masked = nrows < QS || (WIN && key_lo + DKDV_KEYS - 1 > r0 + qoff + win_hi) ||
-                        (LO && key_lo < r0 + QS - 1 + qoff + win_lo);
+                        (LO && key_lo < r0 + QS - 1 + qoff + win_lo) || (DQA && key_lo + DKDV_KEYS > kcap);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
       // dP starts from -D of each element's row, so the MFMAs leave dP - D
@@ -476,7 +527,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             const int kd = key_w + 32 * n - (r0 + rl + qoff);  // key minus the row's diagonal key
-            if ((WIN && kd > win_hi) || (LO && kd < win_lo) || rl >= nrows) {
+            if ((WIN && kd > win_hi) || (LO && kd < win_lo) || rl >= nrows || (DQA && key_w + 32 * n >= kcap)) {
               s[n][i] = 0.f;
               dp[n][i] = 0.f;
             }
@@ -505,6 +556,46 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, DkdvShape<D>::NW == 4 ? 2 : 
                 MF::mfma_acc(dv[n][mt], op, pb[n][c]);
             }
           });
+      if constexpr (DQA) {
+        // dS of this wave's keys into the half's LDS tile [key][query row]:
+        // db[0][c] holds rows 16 c + 4 (lane / 32) + 0..3 and + 8 + 0..3
+        char* dsb = dsbuf + h * DS_BYTES;
+        const int krow = 32 * wv + (lane & 31);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x2_t lo2, hi2;
+          lo2.x = db[0][c].x;
+          lo2.y = db[0][c].y;
+          hi2.x = db[0][c].z;
+          hi2.y = db[0][c].w;
+          *reinterpret_cast<u32x2_t*>(dsb + DsTile::col_off(krow, 16 * c + 4 * (lane >> 5))) = lo2;
+          *reinterpret_cast<u32x2_t*>(dsb + DsTile::col_off(krow, 16 * c + 8 + 4 * (lane >> 5))) = hi2;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the writes landed
+        __builtin_amdgcn_s_barrier();        // every wave's keys are in
+        // dQ (32 rows x 32 features 32 wv ..) += dS (rows x 128 keys) K (keys x features)
+        // wave wv takes feature tile wv (D = 64 has two: waves 2, 3 only
+        // take part in the barriers); all 16 operands are read first
+        // (registers are plentiful at one workgroup per CU)
+        if (wv < NMT) {
+          u32x4_t opa[DKDV_KEYS / 16], opb[DKDV_KEYS / 16];
+#pragma unroll
+          for (int i = 0; i < DKDV_KEYS / 16; ++i) {
+            opa[i] = read_tr_operand(dsb, dsof, 16 * i, 0);  // dS: lanes = query rows, k = keys
+            opb[i] = read_tr_operand(kt, of, 16 * i, wv);    // K: lanes = features, k = keys
+          }
+          f32x16_t qa = zero16();
+#pragma unroll
+          for (int i = 0; i < DKDV_KEYS / 16; ++i) qa = MF::mfma(opa[i], opb[i], qa);
+          const int hq = g * a.group + hh_cur;
+          float* qrow = a.dq_acc + ((q0 + r0) * (int64_t)a.n1 + hq) * D + 32 * wv + (lane & 31);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (rl < nrows) unsafeAtomicAdd(qrow + (int64_t)rl * a.n1 * D, qa[i]);
+          }
+        }
+      }
     }
     stage ^= 1;
   }
@@ -542,14 +633,20 @@ template <typename MF, int D>
 hipError_t launch_dq_t(const BwdArgs& a, int64_t grid, hipStream_t st) {
   return a.seq.seqused_kv ? launch_dq_p<MF, D, true>(a, grid, st) : launch_dq_p<MF, D, false>(a, grid, st);
 }
+template <typename MF, int D, bool PAGED, bool DQA>
+hipError_t launch_dkdv_q(const BwdArgs& a, int64_t grid, hipStream_t st) {
+  constexpr unsigned threads = 64 * DkdvShape<D, DQA>::NW;
+  switch (window_mode(a.seq)) {
+    case 0: k_bwd_dkdv<MF, D, 0, PAGED, DQA><<<(unsigned)grid, threads, 0, st>>>(a); break;
+    case 1: k_bwd_dkdv<MF, D, 1, PAGED, DQA><<<(unsigned)grid, threads, 0, st>>>(a); break;
+    default: k_bwd_dkdv<MF, D, 2, PAGED, DQA><<<(unsigned)grid, threads, 0, st>>>(a); break;
+  }
+  return hipGetLastError();
+}
 template <typename MF, int D, bool PAGED>
 hipError_t launch_dkdv_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
-  constexpr unsigned threads = 64 * DkdvShape<D>::NW;
-  switch (window_mode(a.seq)) {
-    case 0: k_bwd_dkdv<MF, D, 0, PAGED><<<(unsigned)grid, threads, 0, st>>>(a); break;
-    case 1: k_bwd_dkdv<MF, D, 1, PAGED><<<(unsigned)grid, threads, 0, st>>>(a); break;
-    default: k_bwd_dkdv<MF, D, 2, PAGED><<<(unsigned)grid, threads, 0, st>>>(a); break;
-  }
+  if (a.dq_acc) return launch_dkdv_q<MF, D, PAGED, true>(a, grid, st);
+  return launch_dkdv_q<MF, D, PAGED, false>(a, grid, st);
   return hipGetLastError();
 }
 template <typename MF, int D>
@@ -569,6 +666,17 @@ hipError_t launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, hipStrea
     if (head_dim == 128) k_bwd_pre<F16, 128><<<grid, 256, 0, st>>>(a);
     else k_bwd_pre<F16, 64><<<grid, 256, 0, st>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_convert(const float* acc, void* dq, int64_t elems, float sigma, int dtype, hipStream_t st) {
+  const int64_t n8 = elems / 8;
+  if (n8 <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n8 + 255) / 256);
+  if (dtype == 2)
+    k_dq_convert<BF16><<<grid, 256, 0, st>>>(acc, reinterpret_cast<uint16_t*>(dq), n8, sigma);
+  else
+    k_dq_convert<F16><<<grid, 256, 0, st>>>(acc, reinterpret_cast<uint16_t*>(dq), n8, sigma);
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ struct Layout {
   size_t hdr, sq, skv, qbase, kbase, qb_seq, kb_seq;
   size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work, kvbm;
   size_t col_cnt, col_ptr, col_fill, qrows, kvkey0, kvval0, kvkey1, kvval1, kvhist, work_kv;
-  size_t ndl, lse2;
+  size_t ndl, lse2, dq_acc;
   size_t index_end;  // bytes used by the index products
   size_t total;      // bytes needed in all
 };
@@ -134,6 +134,7 @@ struct BwdPreArgs {
   const float* lse;
   float* ndl;   // -rowsum(dO o O)
   float* lse2;  // lse * log2(e)
+  float* dq_acc;  // fp32 dQ accumulator [T_q, N1, D] to clear (atomic dQ), or nullptr
   int64_t rows; // T_q * N1
 };
 
@@ -148,6 +149,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
+  float* dq_acc;  // atomic dQ: fp32 [T_q, N1, D] accumulator of dS K (unscaled), else nullptr
   SeqArgs seq;
   const int32_t* hdr;
   const int32_t* qb_seq;
@@ -176,7 +178,10 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t grid, h
 // e4m3 q / k / v (head dim 128), out in out_dtype
 hipError_t launch_fwd_fp8(const FwdArgs& a, int out_dtype, int64_t grid, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, hipStream_t stream);
+// with a.dq_acc set, the dK/dV kernel also adds dS K into it (atomic dQ)
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t stream);
+// dq = scale * dq_acc in dtype
+hipError_t launch_dq_convert(const float* acc, void* dq, int64_t elems, float sigma, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t stream);
 
 // Profiling hooks (bsa_api.cpp): bracket a launch with events when enabled.

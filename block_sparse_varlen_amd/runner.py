@@ -73,9 +73,10 @@ def ctypes_copy(dst, src):
 class DeviceCase:
     """Inputs resident on the GPU plus output and workspace buffers."""
 
-    def __init__(self, case, device="cuda", with_bwd=None):
+    def __init__(self, case, device="cuda", with_bwd=None, flags=0):
         self.case = case
         self.p = problem_for(case)
+        self.p.flags |= flags  # e.g. BSA_FLAG_DQ_ATOMIC (sizes the workspace too)
         tdt = _TORCH[case.dtype]  # inputs (e4m3 codes as uint8)
         odt = _TORCH[case.out_dtype] if getattr(case, "out_dtype", "") else tdt  # outputs
         self.tdt = tdt

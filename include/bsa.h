@@ -140,6 +140,16 @@ enum { BSA_KV_TND = 0, BSA_KV_PAGED = 1 };
  *   behaviour.  A training step can build the index once and run both passes
  *   on it.  The workspace size rules are unchanged. */
 enum { BSA_FLAG_INDEX_BUILT = 1u };
+/* dQ of bsa_bwd.  By default it comes from a separate Q-block-major pass over
+ * the per-q-block lists (no atomics: bit-identical results run to run).
+ * BSA_FLAG_DQ_ATOMIC instead adds dS K into an fp32 accumulator inside the
+ * KV-major dK/dV kernel with atomics, then scales and converts it (the
+ * workspace grows by T_q * N1 * D * 4 bytes; results vary in the last bits
+ * from run to run, as the FlashAttention UnpaddingScoreGradV2 page says of
+ * its own default).  BSA_FLAG_DETERMINISTIC asks for bit-identical results
+ * run to run and so excludes BSA_FLAG_DQ_ATOMIC (both set:
+ * BSA_ERR_PARAM_INVALID).  Both flags are ignored by bsa_fwd. */
+enum { BSA_FLAG_DETERMINISTIC = 2u, BSA_FLAG_DQ_ATOMIC = 4u };
 
 typedef struct bsa_problem {
   uint32_t struct_size;      /* sizeof(bsa_problem_t) */
@@ -227,8 +237,8 @@ bsa_status_t bsa_fwd_noalloc(const bsa_problem_t* p, const void* q, const void* 
  * key below seqused_kv[b] of every sequence (zeros for keys no row attends)
  * and the rest of the page pool is left as it was; two sequences must not
  * share a page (their gradients would be written, not summed).  dQ is
- * computed by a separate Q-block-major pass, so results are deterministic
- * run to run. */
+ * computed by a separate Q-block-major pass (deterministic run to run)
+ * unless BSA_FLAG_DQ_ATOMIC is set. */
 bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse,
                      const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,

@@ -53,6 +53,19 @@ def status(p, fwd=True, bwd=True):
                                                 ctypes.byref(f) if fwd else None, ctypes.byref(b) if bwd else None)
 
 
+def test_dq_flags():
+    """BSA_FLAG_DQ_ATOMIC adds the fp32 dQ accumulator (T_q * N1 * D * 4
+    bytes) to the backward workspace only; it excludes
+    BSA_FLAG_DETERMINISTIC; unknown flag bits are rejected."""
+    f0, b0 = bsa.bsa_get_workspace_size(good())
+    f1, b1 = bsa.bsa_get_workspace_size(good(flags=bsa.BSA_FLAG_DQ_ATOMIC))
+    assert f1 == f0 and b1 - b0 >= 600 * 4 * 128 * 4 and b1 - b0 < 600 * 4 * 128 * 4 + 256
+    f2, b2 = bsa.bsa_get_workspace_size(good(flags=bsa.BSA_FLAG_DETERMINISTIC))
+    assert (f2, b2) == (f0, b0)
+    assert status(good(flags=bsa.BSA_FLAG_DETERMINISTIC | bsa.BSA_FLAG_DQ_ATOMIC)) == bsa.BSA_ERR_PARAM_INVALID
+    assert status(good(flags=8)) == bsa.BSA_ERR_PARAM_INVALID
+
+
 def test_band_mask_accepted():
     """BSA_MASK_BAND with any pre / next tokens (negative ones included) is a
     valid descriptor; the window does not change the workspace bounds."""
@@ -86,7 +99,7 @@ def test_workspace_size_ok():
     (dict(mask_type=3), bsa.BSA_ERR_PARAM_INVALID),
     (dict(scale=-1.0), bsa.BSA_ERR_PARAM_INVALID),
     (dict(scale=float("nan")), bsa.BSA_ERR_PARAM_INVALID),
-    (dict(flags=2), bsa.BSA_ERR_PARAM_INVALID),  # unknown flag bit
+    (dict(flags=16), bsa.BSA_ERR_PARAM_INVALID),  # unknown flag bit
     (dict(flags=bsa.BSA_FLAG_INDEX_BUILT), bsa.BSA_OK),
     (dict(kv_layout=bsa.BSA_KV_PAGED, page_size=128, max_pages_per_seq=1, page_stride=128 * 2 * 128),
      bsa.BSA_ERR_PARAM_INVALID),  # too few pages per sequence for max_seqlen_kv

@@ -20,6 +20,7 @@ import torch
 
 import oracle
 import synth
+import block_sparse_varlen_amd as bsa
 from block_sparse_varlen_amd.runner import DeviceCase
 
 pytestmark = pytest.mark.gpu
@@ -595,3 +596,51 @@ def test_kv_lists_long_context_equal_mask():
     for nm in ("out", "lse", "dq", "dk", "dv"):
         a, b = getattr(dm, nm), getattr(dc, nm)
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), nm
+
+
+# --------------------------------------------------------------- atomic dQ --
+
+ATOMIC = ["mask_f16_d64_ragged_empty_seq", "mask_gqa_shared_causal", "sabi_messy_causal_by256", "idx_perhead_gqa",
+          "idx_paged_causal_gqa", "mask_bx16_causal", "sabi_bx512_by256_causal", "mask_d64_scale08",
+          "mask_skv0_seq", "idx_band_paged", "mask_by64", "sabi_by48_gqa_paged_f16", "kvidx_messy_perhead_paged"]
+
+
+@pytest.mark.parametrize("name", ATOMIC + ["empty_rows"])
+def test_bwd_small_atomic_dq(name):
+    """dQ accumulated with fp32 atomics inside the dK/dV kernel
+    (BSA_FLAG_DQ_ATOMIC): the same tolerances as the separate pass."""
+    case = BWD[name] if name != "empty_rows" else empty_rows_case()
+    say(f"bwd atomic dQ {name}")
+    dc = DeviceCase(case, with_bwd=True, flags=bsa.BSA_FLAG_DQ_ATOMIC)
+    dc.fwd()
+    nan_fill(dc.dq, dc.dk, dc.dv)
+    dc.bwd()
+    torch.cuda.synchronize()
+    check_bwd(case, dc, tag=name + " atomic")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n", [2, 5])
+def test_bwd_config_atomic_dq(n):
+    """The atomic dQ at full size: sampled q-blocks against the oracle, and
+    dK / dV identical to the separate-pass call's (the flag changes only dQ)."""
+    case = _cfg_bwd(n)
+    say(f"config {n}: bwd with atomic dQ")
+    da = DeviceCase(case, with_bwd=True, flags=bsa.BSA_FLAG_DQ_ATOMIC)
+    db = DeviceCase(case, with_bwd=True)
+    for d in (da, db):
+        d.fwd()
+        d.bwd()
+    torch.cuda.synchronize()
+    assert not torch.isnan(da.dq).any()
+    assert torch.equal(da.dk.view(torch.int16), db.dk.view(torch.int16))
+    assert torch.equal(da.dv.view(torch.int16), db.dv.view(torch.int16))
+    idx = oracle.index_products(case, with_csc=False)
+    rows = _sample_rows(case, idx, 12, 70 + n)
+    rq, _, _ = oracle.backward(case, sample_rows=rows)
+    dq = da.dq.float().cpu().numpy()
+    selq = ~np.isnan(rq[..., 0])
+    eq = rel_fro(dq[selq], rq[selq])
+    eb = rel_fro(db.dq.float().cpu().numpy()[selq], rq[selq])
+    say(f"  config{n}: atomic dQ rel_fro {eq:.3e} (separate pass {eb:.3e})")
+    assert eq <= TOL_G[case.dtype]
