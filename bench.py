@@ -192,13 +192,20 @@ KERNEL_KEYS = {"k_fwd<": "fwd", "k_bwd_dkdv<": "bwd_dkdv", "k_bwd_dq<": "bwd_dq"
 CALIB_BYTES = 512 << 20  # --calib-copy: y = x * 1 over 512 MiB of fp32 (reads and writes that much)
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> None:
-    """Per-launch HBM bytes of each attention kernel from two rocprofv3 --pmc
-    runs of ``bench.py --calib-copy`` (FETCH_SIZE, then WRITE_SIZE, in KiB per
+def short_kernel_name(name: str) -> str:
+    """A rocprofv3 kernel name without namespaces and arguments."""
+    n = name.replace("void ", "").replace("bsa::(anonymous namespace)::", "").replace("bsa::", "")
+    return n.split("(")[0]
+
+
+def write_traffic(fetch_csv: str, write_csv: str, out_path: str = None) -> None:
+    """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs of
+    ``bench.py --calib-copy`` (FETCH_SIZE, then WRITE_SIZE, in KiB per
     dispatch).  Each counter is scaled by bytes / counter of the calibration
-    multiply, whose traffic is known.  Writes TRAFFIC_FILE, keyed by the hash
+    multiply, whose traffic is known.  Writes ``out_path`` (default
+    TRAFFIC_FILE): the attention kernels under the bench's keys, with the hash
     of each kernel's sources so that a later change of a kernel invalidates
-    its entry."""
+    its entry, and every kernel under its own name."""
     import csv
 
     def per_dispatch(path, counter):
@@ -211,10 +218,12 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
             if "MulFunctor" in name:
                 calib.append(v)
                 continue
-            for pat, key in KERNEL_KEYS.items():
-                if pat in name:
-                    tot[key] = tot.get(key, 0.0) + v
-                    disp.setdefault(key, set()).add(r["Dispatch_Id"])
+            keys = [key for pat, key in KERNEL_KEYS.items() if pat in name]
+            if not keys and "bsa::" in name:
+                keys = ["kernel:" + short_kernel_name(name)]
+            for key in keys:
+                tot[key] = tot.get(key, 0.0) + v
+                disp.setdefault(key, set()).add(r["Dispatch_Id"])
         if not calib:
             raise SystemExit(f"{path}: no calibration multiply found (run bench.py with --calib-copy)")
         scale = CALIB_BYTES / (sum(calib) / len(calib) * 1024.0)
@@ -230,7 +239,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
         if k in KERNEL_SOURCES:
             ent["source_sha"] = kernel_source_sha(k)
         out[k] = ent
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(out_path or TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
 
@@ -335,8 +344,8 @@ def fp8_main(args, case, workload):
 
 
 def main():
-    if len(sys.argv) == 4 and sys.argv[1] == "--write-traffic":
-        write_traffic(sys.argv[2], sys.argv[3])
+    if len(sys.argv) in (4, 5) and sys.argv[1] == "--write-traffic":
+        write_traffic(*sys.argv[2:])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +363,8 @@ def main():
                     help="the step lets bsa_fwd and bsa_bwd each build their own block index (no shared build)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 512 MiB elementwise copy (reference for HBM byte counters)")
+    ap.add_argument("--dq-atomic", action="store_true",
+                    help="backward with dQ by fp32 atomics inside the dK/dV kernel (BSA_FLAG_DQ_ATOMIC)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -384,7 +395,7 @@ def main():
     from block_sparse_varlen_amd.runner import DeviceCase
 
     torch.cuda.set_device(0)
-    dc = DeviceCase(case, with_bwd=True)
+    dc = DeviceCase(case, with_bwd=True, flags=bsa.BSA_FLAG_DQ_ATOMIC if args.dq_atomic else 0)
     idx = dc.index(False)
     rcd = visited_rcd(case, idx)
     f_fwd, f_bwd = 4.0 * rcd, 10.0 * rcd
@@ -479,11 +490,14 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    dominant = max((k for k in per_kernel if k in ALG_FLOPS_PER_RCD), key=lambda k: per_kernel[k]["avg_ms"])
-    alg = ALG_FLOPS_PER_RCD[dominant] * rcd
+    # with atomic dQ the dK/dV kernel also does the dQ GEMM, and the "dQ" launch
+    # is the fp32 -> dtype conversion
+    alg_per_rcd = dict(ALG_FLOPS_PER_RCD, bwd_dkdv=10, bwd_dq=0) if args.dq_atomic else ALG_FLOPS_PER_RCD
+    dominant = max((k for k in per_kernel if alg_per_rcd.get(k)), key=lambda k: per_kernel[k]["avg_ms"])
+    alg = alg_per_rcd[dominant] * rcd
     achieved = alg / (per_kernel[dominant]["avg_ms"] * 1e-3) / 1e12
     traffic = None
-    if args.workload == 5 and os.path.exists(TRAFFIC_FILE):
+    if args.workload == 5 and not args.dq_atomic and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
         ent = tr.get(dominant)
@@ -508,7 +522,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f16": "fp16"}[case.dtype],
         "data": "synthetic (seeded N(0,1) Q/K/V/dO, seeded block selection)",
-        "config": {"workload": workload, "global_batch": case.B, "seq_len": int(np.diff(case.cu_q).max()),
+        "config": {"workload": workload + (", dQ by fp32 atomics" if args.dq_atomic else ""),
+                   "global_batch": case.B, "seq_len": int(np.diff(case.cu_q).max()),
                    "heads": case.N1, "head_dim": case.D, "block_shape": [case.bx, case.by],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
