@@ -42,6 +42,8 @@ OTHER_WORKLOADS = {
     3: "sabi block-sparse prefill fwd+bwd: B=1, N=32, S=32768, D=128, bf16, block (128,512), keep U{1..16}",
     4: "GQA + paged-KV block-sparse fwd+bwd: B=8, lengths U{1024..8192}, N1=32, N2=8, D=128, bf16, "
        "128-token pages, idx top-16 (counts U{4..16}), causal",
+    6: "per-token selection fwd+bwd (block shape [1, 128]): TND 2 x 4096, N1=32, N2=8, D=128, bf16, "
+       "idx top-16 per query token (counts U{4..16}), causal",
 }
 # GEMMs each kernel performs out of the counted ones: fwd = QK^T, PV (4 r c D);
 # dK/dV kernel = S, dP, dV, dK (8 r c D); dQ kernel = dQ (2 r c D; its
@@ -353,8 +355,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
-                    help="benchmark configuration (default 5, the long-context workload the metric is quoted on)")
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6],
+                    help="benchmark configuration (default 5, the long-context workload the metric is quoted on; "
+                         "6 = per-token selection, a measurement beside them)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip sampling the graphics clock (always skipped under a profiler)")
     ap.add_argument("--fp8", action="store_true",
@@ -384,7 +387,12 @@ def main():
         torch.cuda.set_device(0)
         fp8_main(args, synth.CONFIGS[args.workload](), workload)
         return
-    case = synth.CONFIGS[args.workload](with_dout=True) if args.workload in (3, 4) else synth.CONFIGS[args.workload]()
+    if args.workload in synth.EXTRA:
+        case = synth.EXTRA[args.workload]()
+    elif args.workload in (3, 4):
+        case = synth.CONFIGS[args.workload](with_dout=True)
+    else:
+        case = synth.CONFIGS[args.workload]()
     cpu = None
     if not args.no_cpu_baseline:
         # before the GPU is touched: the oracle workers fork from this process

@@ -366,6 +366,38 @@ def config5(seed: int = 5, values: bool = True) -> Case:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def config6(seed: int = 6, values: bool = True, with_dout: bool = True) -> Case:
+    """Per-token selection (GenericBlockSparseAttention's default block
+    shape [1, 128]): TND B=2 x 4096 tokens, N1=32, N2=8, D=128, bf16; every
+    query token picks its own KV blocks: idx [8, 8192, 16], count
+    min(U{4..16}, j // 128 + 1) distinct blocks <= its own block, -1 pad;
+    causal.  A measurement workload beside the five benchmark ones."""
+    rng = np.random.default_rng(seed)
+    c = _base("cfg6_per_token", "bf16", 2, 32, 8, 128, 1, 128, "idx", 8, True, False, 0, 1.0 / np.sqrt(128.0))
+    lens = [4096, 4096]
+    c["cu_q"] = _cu(lens)
+    c["cu_kv"] = _cu(lens)
+    tq = sum(lens)
+    idx = np.full((8, tq, 16), -1, dtype=np.int32)
+    cnt = np.zeros((8, tq), dtype=np.int32)
+    for g in range(8):
+        base = 0
+        for L in lens:
+            for j in range(L):
+                top = j // 128 + 1
+                n = min(int(rng.integers(4, 17)), top)
+                idx[g, base + j, :n] = np.sort(rng.choice(top, n, replace=False))
+                cnt[g, base + j] = n
+            base += L
+    c["sparse"] = idx
+    c["count"] = cnt
+    return _finish(rng, c, with_dout, (tq, 8, 128), values=values)
+
+
+# measurement-only workloads (not among the benchmark configurations)
+EXTRA = {6: config6}
+
+
 # --------------------------------------------------------------------------
 # Small randomized cases for parity and edge-case tests.
 # --------------------------------------------------------------------------
