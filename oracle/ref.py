@@ -371,8 +371,9 @@ def backward(case, sample_rows=None, sample_kv=None):
 
     ``sample_rows``: iterable of ``(b, h, qb)`` -- dq only for those q-blocks.
     ``sample_kv``: iterable of ``(b, g, kb)`` -- dk/dv only for those KV
-    blocks.  When either is given the other outputs are NaN where not
-    computed.  With neither, everything is computed.
+    blocks.  When either is given, every output entry that is not computed
+    (dq outside the sampled q-blocks, dk/dv outside the sampled KV blocks'
+    keys) is NaN.  With neither, everything is computed.
     """
     sq, skv, nqb, nkb, qbase, kbase = _blocking(case)
     sigma = scale_of(case.scale, case.D)
@@ -380,8 +381,8 @@ def backward(case, sample_rows=None, sample_kv=None):
     T = int(case.cu_q[-1])
     full = sample_rows is None and sample_kv is None
     dq = np.full((T, case.N1, case.D), 0.0 if full else np.nan)
-    dk = np.zeros(case.k.shape, dtype=np.float64)
-    dv = np.zeros(case.v.shape, dtype=np.float64)
+    dk = np.full(case.k.shape, 0.0 if full else np.nan, dtype=np.float64)
+    dv = np.full(case.v.shape, 0.0 if full else np.nan, dtype=np.float64)
     want_kv = None
     rows = set()
     if full:
@@ -392,6 +393,15 @@ def backward(case, sample_rows=None, sample_kv=None):
         if sample_kv is not None:
             want_kv = set(map(tuple, sample_kv))
             for (b, g, kb) in want_kv:
+                # the sampled blocks' keys start from zero (every other entry stays NaN)
+                keys = np.arange(kb * case.by, min((kb + 1) * case.by, skv[b]))
+                rws, slots = _key_token_rows(case, b, keys)
+                if slots is None:
+                    dk[rws, g] = 0.0
+                    dv[rws, g] = 0.0
+                else:
+                    dk[rws, slots, g] = 0.0
+                    dv[rws, slots, g] = 0.0
                 for h in range(g * G, (g + 1) * G):
                     hs = _sparse_head(case, h)
                     for qb in range(nqb[b]):

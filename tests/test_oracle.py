@@ -514,6 +514,36 @@ def test_empty_rows_and_unreached_keys():
     assert np.all(dk[16:] == 0) and np.all(dv[16:] == 0)
 
 
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sampled_backward_equals_full_and_marks_the_rest(paged):
+    """Sampling q-blocks / KV blocks gives the full backward's values on the
+    sampled entries and NaN on every entry it did not compute."""
+    case = synth.random_case(44, lens_q=[70, 33], lens_kv=[90, 41], N1=4, N2=2, D=8, bx=16, by=32,
+                             kind="mask", sparse_heads=4, causal=True, paged=paged, page_size=16)
+    fq, fk, fv = oracle.backward(case)
+    rows = [(0, 1, 2), (1, 3, 0)]
+    kvs = [(0, 1, 1), (1, 0, 0)]
+    dq, dk, dv = oracle.backward(case, sample_rows=rows, sample_kv=kvs)
+    want_q = np.zeros(dq.shape[:2], dtype=bool)
+    for (b, h, qb) in rows:
+        lo = int(case.cu_q[b]) + qb * case.bx
+        want_q[lo:min(lo + case.bx, int(case.cu_q[b + 1])), h] = True
+    assert np.array_equal(~np.isnan(dq[..., 0]), want_q)
+    np.testing.assert_array_equal(dq[want_q], fq[want_q])
+    skv = case.seqused_kv if case.paged else np.diff(case.cu_kv)
+    want_k = np.zeros(dk.shape[:-1], dtype=bool)
+    for (b, g, kb) in kvs:
+        for j in range(kb * case.by, min(int(skv[b]), (kb + 1) * case.by)):
+            if case.paged:
+                want_k[int(case.block_table[b, j // case.page_size]), j % case.page_size, g] = True
+            else:
+                want_k[int(case.cu_kv[b]) + j, g] = True
+    for got, full in ((dk, fk), (dv, fv)):
+        assert np.array_equal(~np.isnan(got[..., 0]), want_k)
+        np.testing.assert_array_equal(got[want_k], full[want_k])
+
+
 # ---------------------------------------------------------------- invariants --
 
 def test_rows_sum_to_one_via_unit_values():
