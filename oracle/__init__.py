@@ -11,6 +11,7 @@ from .ref import (  # noqa: F401
     selected_blocks,
     visited_blocks,
     index_products,
+    tile_index_products,
     forward,
     backward,
 )

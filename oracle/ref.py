@@ -291,6 +291,87 @@ def index_products(case, with_csc=True):
     return out
 
 
+def tile_index_products(case, tile_rows=128, with_csc=True):
+    """The block index over row tiles of ``tile_rows`` query rows, for
+    selections whose q-blocks are narrower than a tile (``block_x`` divides
+    ``tile_rows``): tile ``t`` of sequence ``b`` holds q-blocks
+    ``t * (tile_rows // bx) ..`` (those below ``nQB_b``) and visits the union
+    of their visited sets :func:`visited_blocks`.  This regrouping is a
+    schedule, not a different method: a query row still attends only to the
+    blocks its own q-block visits, which the row masks record.
+
+    * rows ``r = hs * totalTiles + tbase_b + t`` and the CSR ``row_ptr`` /
+      ``cols`` of the unions, each ascending;
+    * ``row_mask``: ``[nnz, tile_rows // 32]`` uint32 per CSR entry: bit
+      ``i % 32`` of word ``i // 32`` is set when row ``i`` of the tile lies in
+      a q-block of the tile that visits the entry's block (all ``bx`` rows of
+      such a q-block, also any past the sequence end);
+    * ``work``: rows by union size descending, ties by row id;
+    * ``col_ptr`` / ``qrows`` / ``col_mask``: the transpose over tiles, each
+      column's tiles ascending, each entry carrying its tile's row mask for
+      the column's block;
+    * ``work_kv``: as in :func:`index_products`, with tiles in place of
+      q-blocks.
+    """
+    assert tile_rows % case.bx == 0 and tile_rows % 32 == 0
+    per = tile_rows // case.bx
+    nw = tile_rows // 32
+    sq, skv, nqb, nkb, qbase, kbase = _blocking(case)
+    B, Hs = case.B, case.sparse_heads
+    ntile = [_cdiv(s, tile_rows) for s in sq]
+    tbase = [0]
+    for n in ntile:
+        tbase.append(tbase[-1] + n)
+    TT, TKB = tbase[-1], sum(nkb)
+    R = Hs * TT
+    lists, masks = [None] * R, [None] * R
+    for hs in range(Hs):
+        for b in range(B):
+            for t in range(ntile[b]):
+                bits = {}
+                for qb in range(t * per, min((t + 1) * per, nqb[b])):
+                    row0 = (qb - t * per) * case.bx
+                    for kb in visited_blocks(case, b, hs, qb, sq[b], skv[b], nkb[b], qbase[b]):
+                        w = bits.setdefault(kb, [0] * nw)
+                        for i in range(row0, row0 + case.bx):
+                            w[i // 32] |= 1 << (i % 32)
+                r = hs * TT + tbase[b] + t
+                lists[r] = sorted(bits)
+                masks[r] = [bits[kb] for kb in lists[r]]
+    counts = np.array([len(x) for x in lists], dtype=np.int64)
+    row_ptr = np.zeros(R + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    cols = np.array([kb for lst in lists for kb in lst], dtype=np.int64)
+    row_mask = np.array([w for m in masks for w in m], dtype=np.uint32).reshape(-1, nw)
+    work = np.argsort(-counts, kind="stable").astype(np.int64)
+    out = dict(TQB=TT, TKB=TKB, R=R, row_ptr=row_ptr, cols=cols, row_mask=row_mask, work=work, counts=counts)
+    if not with_csc:
+        return out
+    C = Hs * TKB
+    col_lists = [[] for _ in range(C)]
+    for hs in range(Hs):
+        for b in range(B):
+            for t in range(ntile[b]):
+                r = hs * TT + tbase[b] + t
+                for kb, m in zip(lists[r], masks[r]):
+                    col_lists[hs * TKB + kbase[b] + kb].append((t, m))
+    col_cnt = np.array([len(x) for x in col_lists], dtype=np.int64)
+    col_ptr = np.zeros(C + 1, dtype=np.int64)
+    col_ptr[1:] = np.cumsum(col_cnt)
+    srt = [sorted(lst) for lst in col_lists]
+    qrows = np.array([t for lst in srt for t, _ in lst], dtype=np.int64)
+    col_mask = np.array([w for lst in srt for _, m in lst for w in m], dtype=np.uint32).reshape(-1, nw)
+    N2, G = case.N2, case.N1 // case.N2
+    key = np.zeros(N2 * TKB, dtype=np.int64)
+    for g in range(N2):
+        heads = [g] if Hs == N2 else list(range(g * G, (g + 1) * G))
+        for hs in heads:
+            key[g * TKB:(g + 1) * TKB] += col_cnt[hs * TKB:(hs + 1) * TKB]
+    work_kv = np.argsort(-key, kind="stable").astype(np.int64)
+    out.update(C=C, col_ptr=col_ptr, qrows=qrows, col_mask=col_mask, work_kv=work_kv, kv_key=key)
+    return out
+
+
 def _key_token_rows(case, b: int, keys: np.ndarray):
     """Physical location of local keys ``keys`` of sequence ``b``: a TND row
     ``cu_kv[b] + j``, or ``(page, slot) = (block_table[b, j // ps], j % ps)``."""

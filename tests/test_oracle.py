@@ -613,6 +613,85 @@ def test_varlen_equals_per_sequence():
         assert np.array_equal(O1, O[t0:t1]) and np.array_equal(l1, lse[t0:t1])
 
 
+# ------------------------------------------------- tiles of narrow q-blocks --
+
+TILE_CASES = [
+    dict(seed=71, lens_q=[300, 45], N1=4, N2=2, bx=1, by=16, kind="idx", width=6, causal=True),
+    dict(seed=72, lens_q=[150, 97], lens_kv=[260, 97], N1=2, N2=2, bx=4, by=32, kind="mask", causal=True),
+    dict(seed=73, lens_q=[140], N1=2, N2=1, bx=16, by=16, kind="sabi", width=5),
+    dict(seed=74, lens_q=[64, 200], N1=2, N2=2, bx=32, by=16, kind="kvidx", width=9, band=(40, 3)),
+    dict(seed=75, lens_q=[129, 33], N1=2, N2=2, bx=8, by=16, kind="none", causal=True),
+    dict(seed=76, lens_q=[180, 70], N1=4, N2=2, bx=2, by=16, kind="idx_b", width=5, sparse_heads=4),
+]
+
+
+def _tile_case(kw):
+    kw = dict(kw)
+    return synth.random_case(kw.pop("seed"), D=8, with_dout=False, **kw)
+
+
+@pytest.mark.parametrize("ci", range(len(TILE_CASES)))
+def test_tile_index_masks_match_brute_force(ci):
+    """Row-tile index: a row's mask bit for a visited block is set exactly
+    when its q-block holds an allowed (query, key) pair in that block (brute
+    force per token), the union lists are those bits' blocks, and the
+    transpose carries the same masks."""
+    case = _tile_case(TILE_CASES[ci])
+    T = 128
+    ti = oracle.tile_index_products(case, T)
+    pairs = brute.visited_pairs(case)  # (hs, b, qb, kb)
+    sq, skv = brute._lens(case)
+    nqb = [-(-s // case.bx) for s in sq]
+    nt = [-(-s // T) for s in sq]
+    tb = np.concatenate([[0], np.cumsum(nt)]).astype(int)
+    TT = int(tb[-1])
+    per = T // case.bx
+    rp, cols, rm = ti["row_ptr"], ti["cols"], ti["row_mask"]
+    seen = set()
+    for hs in range(case.sparse_heads):
+        for b in range(case.B):
+            for t in range(nt[b]):
+                r = hs * TT + tb[b] + t
+                lst = cols[rp[r]:rp[r + 1]].tolist()
+                assert lst == sorted(set(lst))
+                for e, kb in zip(range(rp[r], rp[r + 1]), lst):
+                    bits = [(int(rm[e, i // 32]) >> (i % 32)) & 1 for i in range(T)]
+                    for i in range(T):
+                        qb = t * per + i // case.bx
+                        want = qb < nqb[b] and (hs, b, qb, kb) in pairs
+                        assert bits[i] == want, (hs, b, t, kb, i)
+                    assert any(bits)
+                    seen |= {(hs, b, t * per + i // case.bx, kb) for i in range(T) if bits[i]}
+    assert seen == pairs
+    cp, qr, cm = ti["col_ptr"], ti["qrows"], ti["col_mask"]
+    assert cp[-1] == rp[-1]
+    TKB = ti["TKB"]
+    nkb = [-(-s // case.by) for s in skv]
+    kbase = np.concatenate([[0], np.cumsum(nkb)]).astype(int)
+    for hs in range(case.sparse_heads):
+        for b in range(case.B):
+            for kb in range(nkb[b]):
+                c = hs * TKB + kbase[b] + kb
+                ts = qr[cp[c]:cp[c + 1]].tolist()
+                assert ts == sorted(set(ts))
+                for o, t in zip(range(cp[c], cp[c + 1]), ts):
+                    r = hs * TT + tb[b] + t
+                    e = rp[r] + cols[rp[r]:rp[r + 1]].tolist().index(kb)
+                    assert np.array_equal(cm[o], rm[e])
+
+
+def test_tile_index_with_whole_tiles_is_the_plain_index():
+    """With block_x equal to the tile, each tile is one q-block: the products
+    are index_products' and every mask word is all ones."""
+    case = _tile_case(dict(seed=77, lens_q=[300, 130], N1=4, N2=2, bx=128, by=32, kind="idx", width=7,
+                           causal=True))
+    a = oracle.index_products(case)
+    t = oracle.tile_index_products(case, 128)
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+        assert np.array_equal(a[k], t[k]), k
+    assert (t["row_mask"] == 0xFFFFFFFF).all() and (t["col_mask"] == 0xFFFFFFFF).all()
+
+
 def test_index_order_and_duplicates_irrelevant():
     case = synth.random_case(61, lens_q=[40, 33], N1=2, D=8, bx=16, by=8, kind="idx", width=8)
     O, lse = oracle.forward(case)
