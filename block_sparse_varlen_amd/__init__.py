@@ -78,7 +78,9 @@ class bsa_problem_t(ctypes.Structure):
 class bsa_index_view_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "off_header", "off_row_ptr", "off_cols", "off_work", "off_col_ptr", "off_qrows", "off_work_kv")] + [
-        (n, ctypes.c_int64) for n in ("max_rows", "max_cols", "max_nnz", "max_kv_items")]
+        (n, ctypes.c_int64) for n in ("max_rows", "max_cols", "max_nnz", "max_kv_items")] + [
+        ("tile_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("off_row_mask", ctypes.c_uint64), ("off_col_mask", ctypes.c_uint64)]
 
 
 def problem(**fields) -> bsa_problem_t:

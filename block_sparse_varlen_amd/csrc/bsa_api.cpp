@@ -101,12 +101,26 @@ bsa_status_t check_bwd_variant(const bsa_problem_t* p) {
   return BSA_OK;
 }
 
+// Whether q-blocks are grouped into row tiles (SeqArgs): narrow q-blocks that
+// divide the tile, a block_y the kernels walk in whole 64-key sub-tiles, and
+// KV blocks few enough for the mask builder's LDS.  (The e4m3 forward keeps
+// per-q-block items.)
+bool row_tiles(const bsa_problem_t* p) {
+  return p->dtype != BSA_DTYPE_FP8_E4M3 && p->block_x <= ROW_TILE_MAX_BX && ROW_TILE % p->block_x == 0 &&
+         p->block_y % 64 == 0 && cdiv64(p->max_seqlen_kv, p->block_y) <= ROW_TILE_MAX_KB;
+}
+// query rows per q-block of the index and of the work items
+int32_t item_rows(const bsa_problem_t* p) { return row_tiles(p) ? ROW_TILE : p->block_x; }
+
 Bounds make_bounds(const bsa_problem_t* p) {
   Bounds b{};
   const int64_t B = p->batch;
-  b.nqb_max = (int32_t)cdiv64(p->max_seqlen_q, p->block_x);
+  const int32_t bx = item_rows(p);
+  b.nqb_max = (int32_t)cdiv64(p->max_seqlen_q, bx);
   b.nkb_max = (int32_t)cdiv64(p->max_seqlen_kv, p->block_y);
-  b.qbar = std::min<int64_t>(p->total_q / p->block_x + B, B * b.nqb_max);
+  b.qbar = std::min<int64_t>(p->total_q / bx + B, B * b.nqb_max);
+  b.qbar_sel = std::max<int64_t>(
+      std::min<int64_t>(p->total_q / p->block_x + B, B * cdiv64(p->max_seqlen_q, p->block_x)), 1);
   if (p->kv_layout == BSA_KV_PAGED)
     b.kbar = B * b.nkb_max;
   else
@@ -116,8 +130,9 @@ Bounds make_bounds(const bsa_problem_t* p) {
   b.rbar = (int64_t)p->sparse_heads * b.qbar;
   b.cbar = (int64_t)p->sparse_heads * b.kbar;
   const int64_t nkb = std::max<int32_t>(b.nkb_max, 1);
-  // per-KV-block lists may select every KV block for one q-block
-  const bool all_kb = p->sparse_kind == BSA_SPARSE_NONE || kv_lists(p->sparse_kind);
+  // per-KV-block lists may select every KV block for one q-block, and a row
+  // tile's union any block
+  const bool all_kb = p->sparse_kind == BSA_SPARSE_NONE || kv_lists(p->sparse_kind) || row_tiles(p);
   b.cmax = (int32_t)(all_kb ? nkb : std::min<int64_t>(p->sparse_width, nkb));
   b.nnzbar = std::max<int64_t>(b.rbar * b.cmax, 1);
   b.kvbar = (int64_t)p->num_heads_kv * b.kbar;
@@ -167,14 +182,20 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   // one radix sort's histograms, or both work lists' side by side
   L.hist = take((size_t)(256 * (cdiv64(b.rbar, 256) + cdiv64(b.kvbar, 256)) + 2) * 4);
   L.work = take((size_t)b.rbar * 4);
-  // per-KV-block lists are scattered into per-row bitmaps first
-  L.kvbm = kv_lists(p->sparse_kind) ? take((size_t)b.rbar * kv_words(b) * 4) : 0;
+  // per-KV-block lists are scattered into per-row bitmaps first (rows of
+  // selection q-blocks)
+  L.kvbm = kv_lists(p->sparse_kind) ? take((size_t)p->sparse_heads * b.qbar_sel * kv_words(b) * 4) : 0;
+  if (row_tiles(p)) {
+    L.qbase_sel = take((B + 1) * 4);
+    L.row_mask = take((size_t)b.nnzbar * 16);
+  }
   if (with_csc) {
     L.col_cnt = take((size_t)b.cbar * 4);
     L.col_ptr = take((size_t)(b.cbar + 1) * 4);
     L.col_fill = take((size_t)b.cbar * 4);
     L.qrows = take((size_t)b.nnzbar * 4);
     L.work_kv = take((size_t)b.kvbar * 4);
+    if (row_tiles(p)) L.col_mask = take((size_t)b.nnzbar * 16);
   }
   L.index_end = off;
   if (with_dl) {
@@ -186,7 +207,7 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   return L;
 }
 
-IndexPtrs make_ptrs(void* ws, const Layout& L, bool with_csc) {
+IndexPtrs make_ptrs(void* ws, const Layout& L, bool with_csc, bool tiles) {
   char* w = static_cast<char*>(ws);
   auto at = [&](size_t o) { return reinterpret_cast<int32_t*>(w + o); };
   IndexPtrs ip{};
@@ -213,6 +234,11 @@ IndexPtrs make_ptrs(void* ws, const Layout& L, bool with_csc) {
     ip.qrows = at(L.qrows);
     ip.work_kv = at(L.work_kv);
   }
+  if (tiles) {
+    ip.qbase_sel = at(L.qbase_sel);
+    ip.row_mask = reinterpret_cast<uint32_t*>(w + L.row_mask);
+    if (with_csc) ip.col_mask = reinterpret_cast<uint32_t*>(w + L.col_mask);
+  }
   return ip;
 }
 
@@ -222,7 +248,8 @@ SeqArgs make_seq(const bsa_problem_t* p, const int64_t* cu_q, const int64_t* cu_
   s.cu_kv = p->kv_layout == BSA_KV_PAGED ? nullptr : cu_kv;
   s.seqused_kv = p->kv_layout == BSA_KV_PAGED ? seqused : nullptr;
   s.batch = p->batch;
-  s.bx = p->block_x;
+  s.bx = item_rows(p);
+  s.sel_bx = p->block_x;
   s.by = p->block_y;
   s.masked = p->mask_type != BSA_MASK_NONE;
   auto clampw = [](int64_t x) { return (int32_t)std::max<int64_t>(-WIN_INF, std::min<int64_t>(WIN_INF, x)); };
@@ -329,7 +356,7 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
   if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const IndexPtrs ip = make_ptrs(workspace, L, false);
+  const IndexPtrs ip = make_ptrs(workspace, L, false, row_tiles(p));
   const int group = p->num_heads_q / p->num_heads_kv;
   const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
   hipError_t e = hipSuccess;
@@ -354,6 +381,9 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
   a.row_ptr = ip.row_ptr;
   a.cols = ip.cols;
   a.work = ip.work;
+  // row tiles without a selection need no row masks: a row's token window
+  // already removes every block its own q-block does not visit
+  a.row_mask = p->sparse_kind != BSA_SPARSE_NONE ? ip.row_mask : nullptr;
   a.n1 = p->num_heads_q;
   a.n2 = p->num_heads_kv;
   a.group = group;
@@ -364,7 +394,7 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
   prof_begin(BSA_KERNEL_FWD, s);
-  const int64_t grid = xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128));
+  const int64_t grid = xcd_grid(b.rbar * a.heads_per_row * cdiv64(item_rows(p), 128));
   e = p->dtype == BSA_DTYPE_FP8_E4M3 ? launch_fwd_fp8(a, p->out_dtype, grid, s)
                                      : launch_fwd(a, p->dtype, p->head_dim, grid, s);
   prof_end(BSA_KERNEL_FWD, s);
@@ -439,6 +469,10 @@ bsa_status_t bsa_index_view(const bsa_problem_t* p, int with_csc, bsa_index_view
   v->max_cols = with_csc ? b.cbar : 0;
   v->max_nnz = b.nnzbar;
   v->max_kv_items = with_csc ? b.kvbar : 0;
+  v->tile_rows = item_rows(p);
+  v->reserved = 0;
+  v->off_row_mask = row_tiles(p) ? L.row_mask : 0;
+  v->off_col_mask = row_tiles(p) && with_csc ? L.col_mask : 0;
   return BSA_OK;
 }
 
@@ -456,7 +490,7 @@ bsa_status_t bsa_build_index(const bsa_problem_t* p, const int64_t* cu_q, const 
   if (!workspace) return BSA_ERR_PARAM_NULLPTR;
   if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const IndexPtrs ip = make_ptrs(workspace, L, with_csc != 0);
+  const IndexPtrs ip = make_ptrs(workspace, L, with_csc != 0, row_tiles(p));
   prof_begin(BSA_KERNEL_INDEX, s);
   const hipError_t e = launch_index(make_seq(p, cu_q, cu_kv, seqused), make_sel(p, sparse, count, workspace, L, b), b, ip,
                                     p->num_heads_kv, p->num_heads_q / p->num_heads_kv, with_csc != 0, s);
@@ -514,7 +548,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const IndexPtrs ip = make_ptrs(workspace, L, true);
+  const IndexPtrs ip = make_ptrs(workspace, L, true, row_tiles(p));
   const int group = p->num_heads_q / p->num_heads_kv;
   const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
   hipError_t e = hipSuccess;
@@ -560,6 +594,8 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.col_ptr = ip.col_ptr;
   a.qrows = ip.qrows;
   a.work_kv = ip.work_kv;
+  a.row_mask = p->sparse_kind != BSA_SPARSE_NONE ? ip.row_mask : nullptr;
+  a.col_mask = p->sparse_kind != BSA_SPARSE_NONE ? ip.col_mask : nullptr;
   a.block_table = block_table;
   a.page_size = p->kv_layout == BSA_KV_PAGED ? p->page_size : 0;
   a.max_pages = p->kv_layout == BSA_KV_PAGED ? p->max_pages_per_seq : 0;
@@ -583,7 +619,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
     if (acc)
       e = launch_dq_convert(acc, dq, p->total_q * p->num_heads_q * p->head_dim, a.sigma, p->dtype, s);
     else
-      e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(p->block_x, 128)), s);
+      e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(item_rows(p), 128)), s);
     prof_end(BSA_KERNEL_BWD_DQ, s);
   }
   return from_hip(e);

@@ -272,6 +272,7 @@ struct RegTileWalk {
   bool grouped;
   int wk;          // grouped: first key of the next window
   uint32_t gmask;  // 16-key groups of the last sub-tile handed out that are selected
+  int ent;         // not grouped: the list entry (CSR position) of the last sub-tile handed out
   int colv;
   // The caller waits for the initial load (any vmcnt wait covering it) before
   // the first take<false>(); take<true>() reads its entries with scalar loads
@@ -325,6 +326,7 @@ struct RegTileWalk {
   __device__ __forceinline__ int take() {
     if (!grouped) {
       const int key = entry<SCALAR>(e) * by + s * T;
+      ent = e;
       ++s;
       if (s >= nsub || key + T >= kend) {
         ++e;

@@ -149,12 +149,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D, a.page_size, a.max_pages, a.page_stride);
   int key_next = 0;
   uint32_t gm_next = 0xFu;  // selected 16-key groups of that sub-tile
+  // row tiles: this wave's 32 rows' bits of that sub-tile's row mask
+  uint32_t rm_next = 0xFFFFFFFFu;
   // the first sub-tile goes out before the block list register has landed
   auto issue = [&](int stage, auto first) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.template take<decltype(first)::value>();
     key_next = key0;
     gm_next = ld.gmask;
+    if (a.row_mask) rm_next = ldu(a.row_mask, (int64_t)ld.ent * 4 + wv);
     const int64_t off = kva.off(key0);
     dma.issue(st, kp + off, it.skv - key0);
     dma.issue(st + TILE, vp + off, it.skv - key0);
@@ -165,18 +168,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   while (more) {
     const int key0 = key_next;     // the sub-tile computed in this step
     const uint32_t gm = gm_next;   // its 16-key groups in selected blocks
+    const uint32_t rm = rm_next;   // its row mask bits of this wave's rows
     wait_vmcnt<0>();               // this wave's loads of the current sub-tile landed
     __builtin_amdgcn_s_barrier();  // everyone's did, and the other buffer is free
     more = ld.valid();
     if (more) issue(stage ^ 1, std::false_type{});
-    if (!wave_active) {
+    if (!wave_active || rm == 0u) {  // (row tiles: no row of this wave selects the sub-tile's block)
       stage ^= 1;
       continue;
     }
     const char* kl = smem + stage * STAGE;
     const char* vl = kl + TILE;
     const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
-    const bool edge = key0 + KT > it.skv || gm != 0xFu ||
+    const bool edge = key0 + KT > it.skv || gm != 0xFu || rm != 0xFFFFFFFFu ||
                       (WIN && key0 + KT - 1 > rw0 + win_hi) || (LO && key0 < rw0 + 31 + win_lo);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // 32-key halves of the sub-tile
@@ -201,6 +205,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (!((gm >> (2 * t + (i >> 3))) & 1u)) s[i] = 0.f;
+        }
+        if (!((rm >> (lane & 31)) & 1u)) {  // row tiles: this row's q-block does not visit the block
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[i] = 0.f;
         }
       }
 #pragma unroll
@@ -428,6 +436,7 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
   ld.open(0);
   ld.settle();
   int r0_next = 0, rend_next = 0, hh_next = 0;
+  uint64_t cm_next = ~0ull;  // row tiles: mask bits of that tile's 64 rows (CSC entry, half)
 
   Dma dma;
   dma.init(qstride);
@@ -440,6 +449,10 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
     r0_next = r0;
     rend_next = ld.row_end();
     hh_next = ld.hh;
+    if (a.col_mask) {
+      const int64_t mo = (int64_t)ld.e * 4 + 2 * ld.half;
+      cm_next = (uint64_t)ldu(a.col_mask, mo) | ((uint64_t)ldu(a.col_mask, mo + 1) << 32);
+    }
     const int nvalid = sq - r0;
     const int64_t off = (q0 + r0) * (int64_t)qstride + (int64_t)h * D;
     dma.issue(st, qp + off, nvalid);
@@ -457,6 +470,7 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
     const int r0 = r0_next;            // the tile computed in this step
     const int nrows = rend_next - r0;  // its rows inside the q-block and the sequence (may exceed QS)
     const int hh_cur = hh_next;        // its q-head within the group
+    const uint64_t cm = cm_next;       // row tiles: its rows' mask bits
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // every wave's loads landed; the other stage is no longer read
     more = ld.valid();
@@ -473,7 +487,13 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
     // (atomic dQ also masks the keys of a partial tile past the block end:
     // their dS would reach dQ)
     const bool masked = nrows < QS || (WIN && key_lo + DKDV_KEYS - 1 > r0 + qoff + win_hi) ||
-                        (LO && key_lo < r0 + QS - 1 + qoff + win_lo) || (DQA && key_lo + DKDV_KEYS > kcap);
+                        (LO && key_lo < r0 + QS - 1 + qoff + win_lo) || (DQA && key_lo + DKDV_KEYS > kcap) ||
+                        cm != ~0ull;
+    // (row tiles: a stage none of whose rows visits the block has nothing to add)
+    if (cm == 0ull) {
+      stage ^= 1;
+      continue;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
       // dP starts from -D of each element's row, so the MFMAs leave dP - D
@@ -527,7 +547,8 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             const int kd = key_w + 32 * n - (r0 + rl + qoff);  // key minus the row's diagonal key
-            if ((WIN && kd > win_hi) || (LO && kd < win_lo) || rl >= nrows || (DQA && key_w + 32 * n >= kcap)) {
+            if ((WIN && kd > win_hi) || (LO && kd < win_lo) || rl >= nrows || (DQA && key_w + 32 * n >= kcap) ||
+                !((cm >> rl) & 1ull)) {
               s[n][i] = 0.f;
               dp[n][i] = 0.f;
             }

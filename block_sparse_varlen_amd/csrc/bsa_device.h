@@ -221,6 +221,11 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return x;
+}
 // Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int l = lane_id();

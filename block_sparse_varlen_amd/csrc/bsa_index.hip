@@ -16,6 +16,10 @@
 //  * CSC col_ptr/qrows: per KV block the ascending q-blocks that visit it (the
 //    per-KV-block layout of GenericBlockSparseAttention's layoutSparsePattern
 //    table), and work_kv: dK/dV items by load, descending.
+//  * Row tiles (SeqArgs.bx = 128 > sel_bx): the "q-blocks" above are tiles of
+//    128 rows, each visiting the union of its selection q-blocks' visited
+//    sets, and every CSR / CSC entry gets a 128-bit row mask of the rows whose
+//    own q-block visits the entry's block (k_tile_masks, k_col_masks).
 //
 // Every product is deterministic: counts come from LDS bitmaps and atomics
 // whose results do not depend on order, the scans are sequential per block,
@@ -71,10 +75,10 @@ __global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs
     return;
   }
   const int B = seq.batch;
-  int carry_q = 0, carry_k = 0;
+  int carry_q = 0, carry_k = 0, carry_s = 0;
   for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
-    int nq = 0, nk = 0;
+    int nq = 0, nk = 0, ns = 0;
     if (b < B) {
       const int sq = (int)(seq.cu_q[b + 1] - seq.cu_q[b]);
       const int skv = seq_kv_len(seq, b);
@@ -82,18 +86,23 @@ __global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs
       ip.skv[b] = skv;
       nq = cdiv(sq, seq.bx);
       nk = cdiv(skv, seq.by);
+      ns = cdiv(sq, seq.sel_bx);
     }
-    int tq, tk;
+    int tq, tk, ts;
     const int iq = block_incl_scan<256>(nq, wsum, tq);
     const int ik = block_incl_scan<256>(nk, wsum, tk);
+    const int is = block_incl_scan<256>(ns, wsum, ts);
     if (b < B) {
       ip.qbase[b] = carry_q + iq - nq;
       ip.kbase[b] = carry_k + ik - nk;
+      if (ip.qbase_sel) ip.qbase_sel[b] = carry_s + is - ns;
     }
     carry_q += tq;
     carry_k += tk;
+    carry_s += ts;
   }
   if (tid == 0) {
+    if (ip.qbase_sel) ip.qbase_sel[B] = carry_s;
     ip.qbase[B] = carry_q;
     ip.kbase[B] = carry_k;
     ip.hdr[H_TQB] = carry_q;
@@ -114,12 +123,118 @@ __global__ __launch_bounds__(256) void k_setup(SeqArgs seq, IndexPtrs ip, int hs
 }
 
 // ------------------------------------------------------- row visited sets --
+// Key-block range of the rows of selection q-block m (sel_bx rows): blocks
+// [kb_lo, nbits) hold keys inside some row's token window.  The rows'
+// allowed key ranges slide up by one key per row, so their union is [first
+// row's lower end, last row's upper end]; an empty window (win_lo > win_hi)
+// leaves no key at all.
+__device__ __forceinline__ void sel_block_range(const SeqArgs& seq, int m, int sq, int skv, int& kb_lo, int& nbits) {
+  const int first_row = m * seq.sel_bx;
+  const int last_row = min((m + 1) * seq.sel_bx, sq) - 1;
+  int lim = skv - 1;
+  int lo = 0;
+  if (seq.masked) {
+    lim = min(lim, last_row + skv - sq + seq.win_hi);
+    lo = max(lo, first_row + skv - sq + seq.win_lo);
+    if (seq.win_lo > seq.win_hi) lim = -1;
+  }
+  nbits = lim < lo ? 0 : lim / seq.by + 1;
+  kb_lo = lim < lo ? 0 : lo / seq.by;
+}
+
+// Row tiles: calls visit(j, kb) for every KV block kb that selection q-block
+// m0 + j (j < nm) of sequence b and sparse head hs selects inside its block
+// range, the wave's lanes striding over (q-block, selection entry) pairs; a
+// block may be visited more than once (duplicate entries).
+template <class F>
+__device__ void tile_members_visit(const SeqArgs& seq, const SelArgs& sel, const IndexPtrs& ip, int hs, int b, int m0,
+                                   int nm, int sq, int skv, F visit) {
+  const int lane = lane_id();
+  const int qs0 = ip.qbase_sel[b];
+  const int nkb_b = cdiv(skv, seq.by);
+  const bool by_block = sel.kind == SP_NONE || kv_lists(sel.kind) || sel.kind == SP_MASK;
+  const int per_m = sel.kind == SP_MASK ? min(sel.width, nkb_b) : by_block ? nkb_b : sel.width;
+  const int total = nm * per_m;
+  for (int x = lane; x < total; x += 64) {
+    const int j = x / per_m, u = x - j * per_m;
+    const int m = m0 + j;
+    int kb_lo, nbits;
+    sel_block_range(seq, m, sq, skv, kb_lo, nbits);
+    int kb = -1;
+    if (sel.kind == SP_NONE) {
+      kb = u;
+    } else if (kv_lists(sel.kind)) {
+      const int64_t row = (int64_t)hs * ip.qbase_sel[seq.batch] + qs0 + m;
+      if ((sel.kvbm[row * sel.kv_words + (u >> 5)] >> (u & 31)) & 1u) kb = u;
+    } else if (sel.kind == SP_MASK || sel.kind == SP_SABI) {
+      if (m < sel.rows) {
+        const int64_t row = (((int64_t)b * sel.hs + hs) * sel.rows + m) * sel.width;
+        if (sel.kind == SP_MASK) {
+          if (reinterpret_cast<const uint8_t*>(sel.sparse)[row + u]) kb = u;
+        } else {
+          const int v = reinterpret_cast<const uint16_t*>(sel.sparse)[row + u];
+          if (v != 0xFFFF) kb = v;
+        }
+      }
+    } else {  // SP_IDX over global selection q-blocks, SP_IDX_B over local ones
+      const bool in_rows = sel.kind == SP_IDX ? qs0 + m < sel.rows : m < sel.rows;
+      if (in_rows) {
+        const int64_t rr = sel.kind == SP_IDX ? (int64_t)hs * sel.rows + qs0 + m
+                                              : ((int64_t)b * sel.hs + hs) * sel.rows + m;
+        const int n = min(max(sel.count[rr], 0), sel.width);
+        if (u < n) kb = reinterpret_cast<const int32_t*>(sel.sparse)[rr * sel.width + u];
+      }
+    }
+    if (kb >= kb_lo && kb < nbits) visit(j, kb);
+  }
+}
+
+// The tile of row r: sparse head, sequence, local tile, lengths and its
+// selection q-blocks m0 .. m0 + nm - 1.
+struct TileRow {
+  int hs, b, t, sq, skv, m0, nm;
+};
+__device__ __forceinline__ TileRow tile_row(const SeqArgs& seq, const IndexPtrs& ip, int r, int TQB) {
+  TileRow w;
+  w.hs = r / TQB;
+  const int qg = r - w.hs * TQB;
+  w.b = ip.qb_seq[qg];
+  w.t = qg - ip.qbase[w.b];
+  w.sq = ip.sq[w.b];
+  w.skv = ip.skv[w.b];
+  const int per = seq.bx / seq.sel_bx;
+  w.m0 = w.t * per;
+  w.nm = min(per, cdiv(w.sq, seq.sel_bx) - w.m0);
+  return w;
+}
+
 // Builds, in the calling wave's LDS words, the bitmap of row r's visited KV
 // blocks and returns the number of bit positions in use (0 for r >= R).  All
 // four waves of the block call it together (it contains block barriers).
 __device__ int row_bitmap(uint32_t* bm, const SeqArgs& seq, const SelArgs& sel, const IndexPtrs& ip,
                           int r, int R, int TQB) {
   const int lane = lane_id();
+  if (ip.qbase_sel) {  // row tiles: the union of the tile's selection q-blocks' visited sets
+    TileRow w{};
+    int nbits = 0;
+    if (r < R) {
+      w = tile_row(seq, ip, r, TQB);
+      for (int j = lane; j < w.nm; j += 64) {
+        int kb_lo, nb;
+        sel_block_range(seq, w.m0 + j, w.sq, w.skv, kb_lo, nb);
+        nbits = max(nbits, nb);
+      }
+      nbits = wave_max_i(nbits);
+    }
+    const int nwords = (nbits + 31) >> 5;
+    for (int x = lane; x < nwords; x += 64) bm[x] = 0u;
+    __syncthreads();
+    if (nbits > 0)
+      tile_members_visit(seq, sel, ip, w.hs, w.b, w.m0, w.nm, w.sq, w.skv,
+                         [&](int, int kb) { atomicOr(&bm[kb >> 5], 1u << (kb & 31)); });
+    __syncthreads();
+    return nbits;
+  }
   int nbits = 0, kb_lo = 0, b = 0, qb = 0, hs = 0, qg = 0;
   if (r < R) {
     hs = r / TQB;
@@ -218,10 +333,12 @@ __global__ __launch_bounds__(256) void k_kv_scatter(SeqArgs seq, SelArgs sel, In
     b = (int)(bh / sel.hs);
     if (kb >= cdiv(ip.skv[b], seq.by)) return;
   }
-  const int nqb = cdiv(ip.sq[b], seq.bx);
+  // bitmap rows are the selection's q-blocks (sel_bx rows each)
+  const int nqb = cdiv(ip.sq[b], seq.sel_bx);
   const int n = min(max(sel.count[L], 0), sel.width);
   const int32_t* lst = reinterpret_cast<const int32_t*>(sel.sparse) + L * sel.width;
-  const int64_t row0 = (int64_t)hs * TQB + ip.qbase[b];
+  const int64_t row0 = ip.qbase_sel ? (int64_t)hs * ip.qbase_sel[seq.batch] + ip.qbase_sel[b]
+                                    : (int64_t)hs * TQB + ip.qbase[b];
   for (int t = lane; t < n; t += 64) {
     const int qb = lst[t];
     if (qb >= 0 && qb < nqb) atomicOr(&sel.kvbm[(row0 + qb) * sel.kv_words + (kb >> 5)], 1u << (kb & 31));
@@ -285,6 +402,64 @@ __global__ __launch_bounds__(256) void k_row_fill(SeqArgs seq, SelArgs sel, Inde
       word &= word - 1;
     }
     pos += __shfl(inc, 63, 64);
+  }
+}
+
+// ------------------------------------------------------------ row masks --
+// Row tiles: the 128-bit row mask of every CSR entry of tile row r (one wave
+// per row, LDS: the position of each KV block in the row's list, then the
+// masks): the rows of each selection q-block of the tile are set in the masks
+// of the blocks it visits.
+__global__ __launch_bounds__(64) void k_tile_masks(SeqArgs seq, SelArgs sel, IndexPtrs ip, int64_t rbar,
+                                                   int nkb_max) {
+  extern __shared__ uint32_t smem_tm[];
+  int* pos = reinterpret_cast<int*>(smem_tm);  // [nkb_max]
+  uint32_t* msk = smem_tm + nkb_max;           // [nkb_max][4]
+  const int lane = lane_id();
+  const int64_t r = blockIdx.x;
+  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB];
+  if (r >= R || r >= rbar) return;
+  const TileRow w = tile_row(seq, ip, (int)r, TQB);
+  const int e0 = ip.row_ptr[r], n = ip.row_ptr[r + 1] - e0;
+  for (int e = lane; e < n; e += 64) {
+    pos[ip.cols[e0 + e]] = e;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) msk[4 * e + x] = 0u;
+  }
+  __syncthreads();
+  // (every block a selection q-block visits is in the row's list: the list is
+  // the union of exactly these visits)
+  tile_members_visit(seq, sel, ip, w.hs, w.b, w.m0, w.nm, w.sq, w.skv, [&](int j, int kb) {
+    const int row0 = j * seq.sel_bx;
+    const uint32_t bits = seq.sel_bx >= 32 ? 0xffffffffu : ((1u << seq.sel_bx) - 1u) << (row0 & 31);
+    atomicOr(&msk[4 * pos[kb] + (row0 >> 5)], bits);
+  });
+  __syncthreads();
+  for (int x = lane; x < 4 * n; x += 64) ip.row_mask[(int64_t)e0 * 4 + x] = msk[x];
+}
+
+// Row tiles: each CSC entry takes the row mask of its (tile, block) CSR entry,
+// found by binary search in the tile's ascending list (one wave per column).
+__global__ __launch_bounds__(256) void k_col_masks(IndexPtrs ip, int64_t cbar) {
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int64_t c = (int64_t)blockIdx.x * 4 + wv;
+  const int C = ip.hdr[H_C], TQB = ip.hdr[H_TQB], TKB = ip.hdr[H_TKB];
+  if (c >= C || c >= cbar) return;
+  const int hs = (int)(c / TKB), kg = (int)(c % TKB);
+  const int b = ip.kb_seq[kg];
+  const int kb = kg - ip.kbase[b];
+  for (int o = ip.col_ptr[c] + lane; o < ip.col_ptr[c + 1]; o += 64) {
+    const int r = hs * TQB + ip.qbase[b] + ip.qrows[o];
+    int lo = ip.row_ptr[r], hi = ip.row_ptr[r + 1];  // cols[lo] <= kb < cols[hi] holds throughout
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ip.cols[mid] <= kb)
+        lo = mid;
+      else
+        hi = mid;
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ip.col_mask[(int64_t)o * 4 + x] = ip.row_mask[(int64_t)lo * 4 + x];
   }
 }
 
@@ -585,7 +760,7 @@ hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd
   const bool merged = with_csc && radix_passes((int64_t)bd.cmax + 1) == 1 &&
                       radix_passes((int64_t)bd.kvkey_max + 1) == 1;
   const bool kv = kv_lists(sel.kind);
-  const int64_t kv_n = kv ? bd.rbar * (int64_t)sel.kv_words : 0;
+  const int64_t kv_n = kv ? (int64_t)sel.hs * bd.qbar_sel * sel.kv_words : 0;
   const unsigned clear_blocks = kv ? (unsigned)std::min<int64_t>(blocks_for(kv_n, 256), 1024) : 0;
   k_setup<<<1 + clear_blocks, 256, 0, st>>>(seq, ip, sel.hs, n2, sel.kvbm, kv_n);
   if (kv) {
@@ -598,6 +773,10 @@ hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd
   k_row_count<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words, bd.cmax, with_csc ? bd.cbar : 0);
   k_scan_excl<<<1, 1024, 0, st>>>(ip.row_cnt, ip.row_ptr, bd.rbar, ip.hdr + H_NNZ);
   k_row_fill<<<rgrid, 256, lds, st>>>(seq, sel, ip, bd.rbar, words, with_csc ? 1 : 0);
+  if (ip.row_mask) {
+    const int nkb = std::max(bd.nkb_max, 1);
+    k_tile_masks<<<(unsigned)bd.rbar, 64, (size_t)nkb * 20, st>>>(seq, sel, ip, bd.rbar, nkb);
+  }
   hipError_t e = hipSuccess;
   if (!merged) {
     e = radix_sort(ip, ip.key0, ip.val0, bd.rbar, (int64_t)bd.cmax + 1, ip.work, st);
@@ -616,6 +795,7 @@ hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd
   if (!direct)
     k_kv_keys<<<blocks_for(bd.kvbar, 256), 256, 0, st>>>(ip, bd.kvbar, sel.hs, n2, group, bd.kvkey_max, kv_key,
                                                          kv_val);
+  if (ip.col_mask) k_col_masks<<<blocks_for(bd.cbar, 4), 256, 0, st>>>(ip, bd.cbar);
   if (!merged) return radix_sort(ip, kv_key, kv_val, bd.kvbar, (int64_t)bd.kvkey_max + 1, ip.work_kv, st);
   const int nba = (int)blocks_for(bd.rbar, 256), nbb = (int)blocks_for(bd.kvbar, 256);
   const SortSeg sa{ip.key0, ip.val0, bd.rbar, ip.hist, nba, ip.work};

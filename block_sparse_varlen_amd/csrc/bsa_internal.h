@@ -22,6 +22,13 @@ enum HeaderSlot {
 enum SparseKind { SP_NONE = 0, SP_MASK = 1, SP_SABI = 2, SP_IDX = 3, SP_IDX_B = 4, SP_KV = 5, SP_KV_B = 6 };
 __host__ __device__ inline bool kv_lists(int kind) { return kind == SP_KV || kind == SP_KV_B; }
 
+// Row tiles: q-blocks of at most ROW_TILE_MAX_BX rows that divide ROW_TILE
+// are grouped into ROW_TILE-row tiles (see SeqArgs), when block_y is a
+// multiple of 64 and a row of the index has at most ROW_TILE_MAX_KB blocks.
+constexpr int ROW_TILE = 128;
+constexpr int ROW_TILE_MAX_BX = 32;
+constexpr int ROW_TILE_MAX_KB = 2048;
+
 // Attention work items are handed to the 8 XCDs in runs of XCD_SEG
 // consecutive items (xcd_item in bsa_attn.h); grids are padded to whole rounds.
 constexpr int NUM_XCD = 8;
@@ -38,6 +45,7 @@ struct Bounds {
   int32_t nqb_max;   // ceil(max_seqlen_q / bx)
   int32_t nkb_max;   // ceil(max_seqlen_kv / by)
   int32_t cmax;      // largest possible visited count of a row
+  int64_t qbar_sel;  // >= total selection q-blocks (block_x rows each; = qbar without row tiles)
   int32_t kvkey_max; // largest possible key of a dK/dV item
 };
 
@@ -47,6 +55,7 @@ struct Layout {
   size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work, kvbm;
   size_t col_cnt, col_ptr, col_fill, qrows, kvkey0, kvval0, kvkey1, kvval1, kvhist, work_kv;
   size_t ndl, lse2, dq_acc;
+  size_t qbase_sel, row_mask, col_mask;  // row tiles only (0 otherwise)
   size_t index_end;  // bytes used by the index products
   size_t total;      // bytes needed in all
 };
@@ -57,7 +66,12 @@ struct SeqArgs {
   const int64_t* cu_kv;       // TND keys, or nullptr when paged
   const int32_t* seqused_kv;  // paged keys, or nullptr
   int32_t batch;
-  int32_t bx, by;
+  // bx: query rows per q-block of the index and of the kernels' work items.
+  // sel_bx: rows per q-block of the caller's selection (block_x).  They differ
+  // only with row tiles: q-blocks of at most 32 rows that divide 128 are
+  // grouped into tiles of bx = 128 rows, each visiting the union of its
+  // q-blocks' visited sets, with per-row masks (row_tiles below).
+  int32_t bx, sel_bx, by;
   // Token window of the causal and band masks: key j is allowed for query i
   // when i + (Skv - Sq) + win_lo <= j <= i + (Skv - Sq) + win_hi (no window:
   // masked = 0).  Causal: win_lo = -WIN_INF, win_hi = 0; band: -preTokens,
@@ -104,6 +118,11 @@ struct IndexPtrs {
   int32_t* col_fill; // [cbar]
   int32_t* qrows;    // [nnzbar]
   int32_t* work_kv;  // [kvbar]
+  // row tiles only (nullptr otherwise):
+  int32_t* qbase_sel;   // [B+1] first global selection q-block of each sequence
+  uint32_t* row_mask;   // [nnzbar][4] per CSR entry: bit i of the 128-bit mask = row i of the tile
+                        //   lies in a q-block that visits the entry's block
+  uint32_t* col_mask;   // [nnzbar][4] the same per CSC entry
 };
 
 struct FwdArgs {
@@ -120,6 +139,7 @@ struct FwdArgs {
   const int32_t* row_ptr;
   const int32_t* cols;
   const int32_t* work;
+  const uint32_t* row_mask;  // row tiles with a selection: [nnz][4] per CSR entry, else nullptr
   int32_t n1, n2, group;   // N1, N2, G = N1/N2
   int32_t heads_per_row;   // G when the selection is shared by a GQA group, else 1
   int32_t page_size, max_pages;
@@ -162,6 +182,8 @@ struct BwdArgs {
   const int32_t* col_ptr;
   const int32_t* qrows;
   const int32_t* work_kv;
+  const uint32_t* row_mask;    // row tiles with a selection: [nnz][4] per CSR entry, else nullptr
+  const uint32_t* col_mask;    // the same per CSC entry
   const int32_t* block_table;  // paged K/V (and dK/dV): [B, max_pages]
   int32_t page_size, max_pages;
   int64_t page_stride;     // elements

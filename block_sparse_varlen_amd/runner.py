@@ -150,8 +150,12 @@ class DeviceCase:
         hdr = arr(v.off_header, 8)
         tqb, tkb, R, C, nnz, kvi = (int(x) for x in hdr[:6])
         out = dict(TQB=tqb, TKB=tkb, R=R, nnz=nnz, row_ptr=arr(v.off_row_ptr, R + 1),
-                   cols=arr(v.off_cols, nnz), work=arr(v.off_work, R))
+                   cols=arr(v.off_cols, nnz), work=arr(v.off_work, R), tile_rows=int(v.tile_rows))
+        if v.off_row_mask:
+            out["row_mask"] = arr(v.off_row_mask, 4 * nnz).view(np.uint32).reshape(-1, 4)
         if with_csc:
             out.update(C=C, col_ptr=arr(v.off_col_ptr, C + 1), qrows=arr(v.off_qrows, nnz),
                        work_kv=arr(v.off_work_kv, kvi))
+            if v.off_col_mask:
+                out["col_mask"] = arr(v.off_col_mask, 4 * nnz).view(np.uint32).reshape(-1, 4)
         return out

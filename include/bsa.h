@@ -262,11 +262,24 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
  *   work_kv[N2*totalKBlocks]: items g*totalKBlocks + kbase_b + kb by the number
  *                 of (sparse head of group g, q-block) pairs reaching them,
  *                 descending, ties by item id.
+ * Row tiles: when block_x is at most 32 and divides 128, block_y is a
+ * multiple of 64, the dtype is fp16 or bf16 and ceil(max_seqlen_kv / block_y)
+ * <= 2048, the index groups the selection's q-blocks into tiles of
+ * tile_rows = 128 query rows (tile t of sequence b holds q-blocks
+ * t*128/block_x ..), and every "q-block" above is a tile: a tile visits the
+ * union of its q-blocks' visited sets, and each CSR entry (and each CSC
+ * entry, with_csc) carries a 128-bit row mask, uint32 [4] (bit i%32 of word
+ * i/32: row i of the tile lies in one of the tile's q-blocks that visits the
+ * entry's block).  The attention kernels then take whole tiles of rows as
+ * work items instead of q-blocks of block_x rows, and mask per row.
  * The workspace needed is at most bsa_get_workspace_size's fwd_bytes
  * (with_csc == 0) or bwd_bytes (with_csc != 0). */
 typedef struct bsa_index_view {
   uint64_t off_header, off_row_ptr, off_cols, off_work, off_col_ptr, off_qrows, off_work_kv;
   int64_t max_rows, max_cols, max_nnz, max_kv_items;
+  int32_t tile_rows;  /* query rows per q-block of the index (block_x, or 128 with row tiles) */
+  int32_t reserved;
+  uint64_t off_row_mask, off_col_mask;  /* row tiles: uint32 [nnz][4] per CSR / CSC entry, else 0 */
 } bsa_index_view_t;
 
 bsa_status_t bsa_index_view(const bsa_problem_t* p, int with_csc, bsa_index_view_t* view);

@@ -134,6 +134,25 @@ def fwd_cases():
                                    sparse_heads=2, by=80, paged=True, causal=True, messy=True),
         "none_by16_band": R(142, lens_q=[260, 100], N1=2, D=64, kind="none", by=16, band=(100, 17)),
         "kvidx_by32_bx32": R(143, lens_q=[350, 123], lens_kv=[400, 150], N1=2, D=128, kind="kvidx", bx=32, by=32),
+        # q-blocks of 1 .. 32 rows grouped into 128-row tiles with row masks:
+        # per-token top-k (GenericBlockSparseAttention's default [1, 128]
+        # block shape), every selection form, paged, band, short selection
+        # tensors, sequences shorter than a tile and empty ones
+        "tile_idx_bx1_gqa_causal": R(144, lens_q=[1500, 37, 0, 700], N1=4, N2=2, D=128, kind="idx",
+                                     sparse_heads=2, bx=1, by=64, width=5, causal=True),
+        "tile_mask_bx2_perhead_band": R(145, lens_q=[333, 200], lens_kv=[500, 180], N1=4, N2=2, D=64,
+                                        kind="mask", sparse_heads=4, bx=2, by=64, density=0.3, band=(150, 20)),
+        "tile_sabi_bx4_messy_f16": R(146, lens_q=[290, 131], N1=2, D=64, dtype="f16", kind="sabi", bx=4,
+                                     messy=True, causal=True),
+        "tile_idx_b_bx8_paged": R(147, lens_q=[400, 257], lens_kv=[520, 300], N1=4, N2=2, D=128, kind="idx_b",
+                                  sparse_heads=2, bx=8, paged=True, messy=True),
+        "tile_kvidx_bx16_causal": R(148, lens_q=[380, 250], N1=2, D=128, kind="kvidx", bx=16, causal=True),
+        "tile_kvidx_b_bx32_gqa_f16": R(149, lens_q=[300, 90], lens_kv=[640, 200], N1=4, N2=2, D=128,
+                                       dtype="f16", kind="kvidx_b", sparse_heads=2, bx=32, messy=True),
+        "tile_none_bx1_sq_lt_skv": R(150, lens_q=[150, 70], lens_kv=[700, 400], N1=2, D=64, kind="none", bx=1,
+                                     causal=True),
+        "tile_idx_bx1_short_rows": _short_idx(R(151, lens_q=[260, 200], N1=2, D=128, kind="idx", bx=1, width=4,
+                                                causal=True), 300),
     }
 
 
@@ -223,6 +242,22 @@ def bwd_cases():
         "idx_by80_band": R(240, lens_q=[520, 300], lens_kv=[700, 310], N1=4, N2=2, D=128, kind="idx",
                            sparse_heads=4, by=80, band=(200, 30)),
         "sabi_by192_causal": R(241, lens_q=[700, 400], N1=2, D=128, kind="sabi", by=192, causal=True),
+        # row tiles (q-blocks of 1 .. 32 rows): the dK/dV stages take the
+        # column masks, the dQ pass the row masks
+        "tile_idx_bx1_gqa_causal": R(242, lens_q=[1500, 37, 0, 700], N1=4, N2=2, D=128, kind="idx",
+                                     sparse_heads=2, bx=1, by=64, width=5, causal=True),
+        "tile_mask_bx2_perhead_band_f16": R(243, lens_q=[333, 200], lens_kv=[500, 180], N1=4, N2=2, D=64,
+                                            dtype="f16", kind="mask", sparse_heads=4, bx=2, by=64, density=0.3,
+                                            band=(150, 20)),
+        "tile_sabi_bx4_messy": R(244, lens_q=[290, 131], N1=2, D=128, kind="sabi", bx=4, messy=True, causal=True),
+        "tile_idx_b_bx8_paged": R(245, lens_q=[400, 257], lens_kv=[520, 300], N1=4, N2=2, D=128, kind="idx_b",
+                                  sparse_heads=2, bx=8, paged=True, messy=True),
+        "tile_kvidx_bx16_by256": R(246, lens_q=[380, 250], lens_kv=[700, 250], N1=2, D=128, kind="kvidx", bx=16,
+                                   by=256, causal=True),
+        "tile_kvidx_b_bx32_gqa": R(247, lens_q=[300, 90], lens_kv=[640, 200], N1=4, N2=2, D=64,
+                                   kind="kvidx_b", sparse_heads=2, bx=32, messy=True),
+        "tile_none_bx1_sq_lt_skv": R(248, lens_q=[150, 70], lens_kv=[700, 400], N1=2, D=128, kind="none", bx=1,
+                                     causal=True),
     }
 
 
@@ -319,9 +354,14 @@ def test_index_bit_exact(name):
     say(f"index {name}")
     dc = DeviceCase(case, with_bwd=True)
     got = dc.index(True)
-    ref = oracle.index_products(case, with_csc=True)
+    keys = ["row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"]
+    if got["tile_rows"] != case.bx:  # narrow q-blocks grouped into row tiles
+        ref = oracle.tile_index_products(case, got["tile_rows"], with_csc=True)
+        keys += ["row_mask", "col_mask"]
+    else:
+        ref = oracle.index_products(case, with_csc=True)
     assert got["R"] == ref["R"]
-    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv"):
+    for k in keys:
         assert np.array_equal(got[k], ref[k]), k
 
 
