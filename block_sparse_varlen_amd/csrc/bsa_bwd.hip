@@ -489,11 +489,6 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
     const bool masked = nrows < QS || (WIN && key_lo + DKDV_KEYS - 1 > r0 + qoff + win_hi) ||
                         (LO && key_lo < r0 + QS - 1 + qoff + win_lo) || (DQA && key_lo + DKDV_KEYS > kcap) ||
                         cm != ~0ull;
-    // (row tiles: a stage none of whose rows visits the block has nothing to add)
-    if (cm == 0ull) {
-      stage ^= 1;
-      continue;
-    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 32-row halves of the tile
       // dP starts from -D of each element's row, so the MFMAs leave dP - D
@@ -541,6 +536,8 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
         }
       }
       if (masked) {  // edge tiles only: P = dS = 0 past the sequence end or outside the window
+        // row tiles: bit 8 (i / 4) + i % 4 of lm is the mask bit of element i's row
+        const uint32_t lm = (uint32_t)(cm >> (32 * h)) >> (4 * (lane >> 5));
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int rl = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
@@ -548,7 +545,7 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
           for (int n = 0; n < NT; ++n) {
             const int kd = key_w + 32 * n - (r0 + rl + qoff);  // key minus the row's diagonal key
             if ((WIN && kd > win_hi) || (LO && kd < win_lo) || rl >= nrows || (DQA && key_w + 32 * n >= kcap) ||
-                !((cm >> rl) & 1ull)) {
+                !((lm >> (8 * (i >> 2) + (i & 3))) & 1u)) {
               s[n][i] = 0.f;
               dp[n][i] = 0.f;
             }
