@@ -591,6 +591,47 @@ def test_bwd_config(n):
     assert eq <= tol and ek <= tol and ev <= tol
 
 
+# ------------------------------------------ per-token selection, full size --
+
+@pytest.mark.timeout(900)
+def test_per_token_workload_full_size():
+    """GenericBlockSparseAttention's default [1, 128] block shape at the
+    bench's per-token workload size (2 x 4096 tokens, 32/8 heads, top-16 per
+    token, causal), run as 128-row tiles: the tile index bit-exact (masks
+    included), sampled tokens' O / lse / dQ and sampled KV blocks' dK / dV
+    against the oracle."""
+    say("per-token workload: generating")
+    case = synth.config6()
+    dc = DeviceCase(case, with_bwd=True)
+    dc.fwd()
+    nan_fill(dc.dq, dc.dk, dc.dv)
+    dc.bwd()
+    torch.cuda.synchronize()
+    assert not torch.isnan(dc.out).any() and not torch.isnan(dc.dq).any()
+    assert not torch.isnan(dc.dk).any() and not torch.isnan(dc.dv).any()
+    got = dc.index(True)
+    assert got["tile_rows"] == 128
+    ref = oracle.tile_index_products(case, 128, with_csc=True)
+    for k in ("row_ptr", "cols", "work", "col_ptr", "qrows", "work_kv", "row_mask", "col_mask"):
+        assert np.array_equal(got[k], ref[k]), k
+    rng = np.random.default_rng(66)
+    rows = {(int(rng.integers(2)), int(rng.integers(32)), int(rng.integers(4096))) for _ in range(30)}
+    rows |= {(0, 0, 0), (1, 31, 4095), (0, 5, 127), (1, 9, 128)}
+    rows = sorted(rows)
+    check_fwd(case, dc, sample=rows, tag="per-token")
+    kvs = [(0, 2, 31), (1, 6, 20)]
+    rq, rk, rv = oracle.backward(case, sample_rows=rows[:10], sample_kv=kvs)
+    dq = dc.dq.float().cpu().numpy()
+    dk = dc.dk.float().cpu().numpy()
+    dv = dc.dv.float().cpu().numpy()
+    selq = ~np.isnan(rq[..., 0])
+    selk = ~np.isnan(rk[..., 0])
+    eq, ek, ev = rel_fro(dq[selq], rq[selq]), rel_fro(dk[selk], rk[selk]), rel_fro(dv[selk], rv[selk])
+    say(f"  per-token: rel_fro dq={eq:.3e} dk={ek:.3e} dv={ev:.3e} (sampled)")
+    tol = TOL_G[case.dtype]
+    assert eq <= tol and ek <= tol and ev <= tol
+
+
 # ------------------------------------------- per-KV-block lists at full size --
 
 def _kv_lists_of_mask(m):
