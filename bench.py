@@ -555,6 +555,15 @@ def main():
                   "frac_of_peak_at_sclk": round(total_tflops / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4) if sclk else None},
         "cpu_baseline": cpu,
     }
+    if case.causal and case.sparse_kind == "none" and case.band is None:
+        # dense causal: the token-exact count 4 D N1 sum_b Sq_b (Sq_b + 1) / 2 beside
+        # the per-visited-block one (diagonal blocks counted whole)
+        sq = np.diff(case.cu_q).astype(np.float64)
+        fe = 4.0 * case.D * case.N1 * float((sq * (sq + 1) / 2).sum())
+        line["causal_exact"] = {"fwd_flops": fe, "bwd_flops": 2.5 * fe,
+                                "step_tflops": round(3.5 * fe / (ms_step * 1e-3) / 1e12, 3),
+                                "fwd_call_tflops": round(fe / (fwd_call["median"] * 1e-3) / 1e12, 3),
+                                "bwd_call_tflops": round(2.5 * fe / (bwd_call["median"] * 1e-3) / 1e12, 3)}
     print(json.dumps(line), flush=True)
 
 
