@@ -258,6 +258,14 @@ def bwd_cases():
                                    kind="kvidx_b", sparse_heads=2, bx=32, messy=True),
         "tile_none_bx1_sq_lt_skv": R(248, lens_q=[150, 70], lens_kv=[700, 400], N1=2, D=128, kind="none", bx=1,
                                      causal=True),
+        "tile_mask_bx16_skv0_seq": R(249, lens_q=[300, 200, 150], lens_kv=[400, 0, 260], N1=2, D=64, kind="mask",
+                                     bx=16, density=0.3),
+        "tile_none_bx4_band_empty_window": R(250, lens_q=[300, 150], N1=2, D=64, kind="none", bx=4, band=(4, -9)),
+        "tile_sabi_bx8_paged_ps64_gqa_f16": R(251, lens_q=[333, 260], lens_kv=[400, 512], N1=4, N2=2, D=128,
+                                              dtype="f16", kind="sabi", sparse_heads=2, bx=8, paged=True,
+                                              page_size=64, causal=True),
+        "tile_idx_bx32_short_rows_perhead": _short_idx(R(252, lens_q=[600, 400], N1=4, N2=2, D=64, kind="idx",
+                                                         sparse_heads=4, bx=32, width=5), 20),
     }
 
 
@@ -403,7 +411,7 @@ def test_bwd_small(name):
     check_bwd(case, dc, tag=name)
 
 
-@pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_perhead_gqa"])
+@pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_perhead_gqa", "tile_idx_bx1_gqa_causal"])
 def test_bwd_deterministic(name):
     case = BWD[name]
     dc = DeviceCase(case, with_bwd=True)
@@ -418,7 +426,8 @@ def test_bwd_deterministic(name):
 
 # ------------------------------------------------------- prebuilt index --
 
-@pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_paged_causal_gqa", "sabi_bx512_by256_causal"])
+@pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_paged_causal_gqa", "sabi_bx512_by256_causal",
+                                  "tile_idx_b_bx8_paged"])
 def test_prebuilt_index(name):
     """bsa_build_index (with the transposed lists) once, then bsa_fwd and
     bsa_bwd with BSA_FLAG_INDEX_BUILT: same results as self-indexing calls,
@@ -453,7 +462,7 @@ def _guarded(like, guard, fill):
 
 
 @pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_paged_causal_gqa", "mask_bx192_paged",
-                                  "mask_f16_d64_ragged_empty_seq"])
+                                  "mask_f16_d64_ragged_empty_seq", "tile_mask_bx2_perhead_band_f16"])
 def test_no_writes_outside_buffers(name):
     """Outputs and workspace sit between guard regions (NaN, or a byte pattern
     for the workspace); a forward and a backward call leave every guard as it
@@ -683,7 +692,8 @@ def test_kv_lists_long_context_equal_mask():
 
 ATOMIC = ["mask_f16_d64_ragged_empty_seq", "mask_gqa_shared_causal", "sabi_messy_causal_by256", "idx_perhead_gqa",
           "idx_paged_causal_gqa", "mask_bx16_causal", "sabi_bx512_by256_causal", "mask_d64_scale08",
-          "mask_skv0_seq", "idx_band_paged", "mask_by64", "sabi_by48_gqa_paged_f16", "kvidx_messy_perhead_paged"]
+          "mask_skv0_seq", "idx_band_paged", "mask_by64", "sabi_by48_gqa_paged_f16", "kvidx_messy_perhead_paged",
+          "tile_idx_bx1_gqa_causal", "tile_kvidx_bx16_by256", "tile_none_bx1_sq_lt_skv", "tile_mask_bx16_skv0_seq"]
 
 
 @pytest.mark.parametrize("name", ATOMIC + ["empty_rows"])

@@ -49,6 +49,9 @@ def test_noalloc_matches_workspace_entry_point():
     _same(small, "small")
     # and the long-context workload's shape of index (block-causal mask)
     _same(synth.config1(), "tiny")
+    # per-token selection as 128-row tiles (row masks in the scratch index)
+    _same(synth.random_case(303, lens_q=[700, 129], N1=4, N2=2, D=128, kind="idx", sparse_heads=2, bx=1, width=5,
+                            causal=True, with_dout=False), "row tiles")
 
 
 def test_noalloc_rejects_oversize_problem():
