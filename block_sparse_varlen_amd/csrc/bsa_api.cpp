@@ -103,11 +103,10 @@ bsa_status_t check_bwd_variant(const bsa_problem_t* p) {
 
 // Whether q-blocks are grouped into row tiles (SeqArgs): narrow q-blocks that
 // divide the tile, a block_y the kernels walk in whole 64-key sub-tiles, and
-// KV blocks few enough for the mask builder's LDS.  (The e4m3 forward keeps
-// per-q-block items.)
+// KV blocks few enough for the mask builder's LDS.
 bool row_tiles(const bsa_problem_t* p) {
-  return p->dtype != BSA_DTYPE_FP8_E4M3 && p->block_x <= ROW_TILE_MAX_BX && ROW_TILE % p->block_x == 0 &&
-         p->block_y % 64 == 0 && cdiv64(p->max_seqlen_kv, p->block_y) <= ROW_TILE_MAX_KB;
+  return p->block_x <= ROW_TILE_MAX_BX && ROW_TILE % p->block_x == 0 && p->block_y % 64 == 0 &&
+         cdiv64(p->max_seqlen_kv, p->block_y) <= ROW_TILE_MAX_KB;
 }
 // query rows per q-block of the index and of the work items
 int32_t item_rows(const bsa_problem_t* p) { return row_tiles(p) ? ROW_TILE : p->block_x; }

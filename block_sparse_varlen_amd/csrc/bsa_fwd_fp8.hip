@@ -134,11 +134,14 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   kva.init(a.seq, a.block_table, it.b, it.g, a.n2, D / 2, a.page_size, a.max_pages, a.page_stride / 2);
   int key_next = 0;
   uint32_t gm_next = 0xFu;  // selected 16-key groups of that sub-tile
+  // row tiles: this wave's 32 rows' bits of that sub-tile's row mask
+  uint32_t rm_next = 0xFFFFFFFFu;
   auto issue = [&](int stage, auto first) {
     char* st = smem + stage * STAGE;
     const int key0 = ld.template take<decltype(first)::value>();
     key_next = key0;
     gm_next = ld.gmask;
+    if (a.row_mask) rm_next = ldu(a.row_mask, (int64_t)ld.ent * 4 + wv);
     const int64_t off = kva.off(key0);
     kdma.issue(st, kbase_p + off, it.skv - key0);
     vdma.issue(st + TILE, vbase_p + off, it.skv - key0);
@@ -149,12 +152,13 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   while (more) {
     const int key0 = key_next;
     const uint32_t gm = gm_next;   // its 16-key groups in selected blocks
+    const uint32_t rm = rm_next;   // its row mask bits of this wave's rows
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     more = ld.valid();
     if (more) issue(stage ^ 1, std::false_type{});
     settle_scalar_loads();
-    if (!wave_active) {
+    if (!wave_active || rm == 0u) {  // (row tiles: no row of this wave selects the sub-tile's block)
       stage ^= 1;
       continue;
     }
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
     }
     // ---- masks: keys past Skv, outside the rows' windows (edge sub-tiles only) ----
     const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
-    const bool edge = key0 + KT > it.skv || gm != 0xFu ||
+    const bool edge = key0 + KT > it.skv || gm != 0xFu || rm != 0xFFFFFFFFu ||
                       (WIN && key0 + KT - 1 > rw0 + win_hi) || (LO && key0 < rw0 + 31 + win_lo);
     if (edge) {
       const int lim = WIN ? min(it.skv - 1, my_row + qoff + win_hi) : it.skv - 1;
@@ -198,6 +202,12 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (!((gm >> (2 * t + (i >> 3))) & 1u)) s[t][i] = -INFINITY;
+      }
+      if (!((rm >> (lane & 31)) & 1u)) {  // row tiles: this row's q-block does not visit the block
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[t][i] = -INFINITY;
       }
     }
     // ---- online softmax (row = this lane's column) ----

@@ -264,8 +264,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
  *                 of (sparse head of group g, q-block) pairs reaching them,
  *                 descending, ties by item id.
  * Row tiles: when block_x is at most 32 and divides 128, block_y is a
- * multiple of 64, the dtype is fp16 or bf16 and ceil(max_seqlen_kv / block_y)
- * <= 2048, the index groups the selection's q-blocks into tiles of
+ * multiple of 64 and ceil(max_seqlen_kv / block_y) <= 2048, the index groups the selection's q-blocks into tiles of
  * tile_rows = 128 query rows (tile t of sequence b holds q-blocks
  * t*128/block_x ..), and every "q-block" above is a tile: a tile visits the
  * union of its q-blocks' visited sets, and each CSR entry (and each CSC

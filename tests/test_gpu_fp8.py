@@ -42,6 +42,11 @@ def cases():
         # 48-key blocks: 64-key windows with masked groups
         "mask_by48_paged": R(410, lens_q=[300, 200], lens_kv=[333, 450], N1=4, N2=2, kind="mask", by=48,
                              paged=True, out_dtype="bf16", **F),
+        # per-token selection as 128-row tiles with row masks
+        "tile_idx_bx1_gqa_causal": R(411, lens_q=[700, 129], N1=4, N2=2, kind="idx", sparse_heads=2, bx=1,
+                                     width=5, causal=True, out_dtype="bf16", **F),
+        "tile_mask_bx8_band_f16": R(412, lens_q=[333, 200], lens_kv=[500, 250], N1=2, kind="mask", bx=8, by=64,
+                                    density=0.4, band=(150, 20), out_dtype="f16", **F),
     }
 
 
