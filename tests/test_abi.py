@@ -193,6 +193,28 @@ def test_index_view_is_consistent_with_sizes():
     assert v0.max_rows >= 4 * (600 // 128 + 2)
 
 
+def test_index_view_reports_row_tiles():
+    """q-blocks of at most 32 rows that divide 128 are indexed as 128-row
+    tiles with row masks (block_y a multiple of 64, at most 2048 KV blocks a
+    sequence); everything else keeps its own q-blocks and no masks."""
+    def view(with_csc=True, **kw):
+        return bsa.bsa_index_view(good(**kw), with_csc)
+
+    for bx in (1, 2, 4, 8, 16, 32):
+        v = view(block_x=bx, sparse_kind=bsa.BSA_SPARSE_IDX_I32, sparse_rows=600, sparse_width=8)
+        assert v.tile_rows == 128, bx
+        assert v.off_row_mask and v.off_col_mask
+        assert v.off_row_mask + 16 * v.max_nnz <= bsa.bsa_get_workspace_size(good(block_x=bx))[1]
+        assert view(False, block_x=bx).off_col_mask == 0  # no transposed lists, no column masks
+        assert view(block_x=bx, dtype=bsa.BSA_DTYPE_FP8_E4M3,
+                    out_dtype=bsa.BSA_DTYPE_BF16).tile_rows == 128  # the e4m3 forward too
+    for kw in (dict(block_x=128), dict(block_x=64), dict(block_x=48), dict(block_x=24),
+               dict(block_x=16, block_y=48), dict(block_x=1, block_y=16),
+               dict(block_x=1, block_y=64, max_seqlen_kv=64 * 2049, total_kv=64 * 2049 + 200)):
+        v = view(**kw)
+        assert v.tile_rows == kw["block_x"] and v.off_row_mask == 0 and v.off_col_mask == 0, kw
+
+
 def test_fp8_forward_only():
     """e4m3 inputs: forward with an fp16 / bf16 out_dtype and head dim 128;
     no backward variant; head dim 64 has no compiled variant."""
