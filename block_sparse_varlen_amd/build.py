@@ -59,6 +59,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking libbsa.so failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    # a C++ caller of the ABI alone (tests/c/abi_check.cpp), linked to this library
+    exe = os.path.join(HERE, "abi_check")
+    cmd = [_hipcc(), "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_check.cpp"), "-L", HERE, "-lbsa", "-Wl,-rpath,$ORIGIN", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building abi_check failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     if verbose:
         print(f"built {OUT}")
     return OUT
