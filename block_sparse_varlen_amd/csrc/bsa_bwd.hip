@@ -665,7 +665,6 @@ template <typename MF, int D, bool PAGED>
 hipError_t launch_dkdv_p(const BwdArgs& a, int64_t grid, hipStream_t st) {
   if (a.dq_acc) return launch_dkdv_q<MF, D, PAGED, true>(a, grid, st);
   return launch_dkdv_q<MF, D, PAGED, false>(a, grid, st);
-  return hipGetLastError();
 }
 template <typename MF, int D>
 hipError_t launch_dkdv_t(const BwdArgs& a, int64_t grid, hipStream_t st) {

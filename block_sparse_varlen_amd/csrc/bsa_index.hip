@@ -623,17 +623,6 @@ __device__ __forceinline__ void row_coords(const IndexPtrs& ip, int r, int TQB, 
   qb = qg - ip.qbase[b];
 }
 
-__global__ __launch_bounds__(256) void k_col_count(IndexPtrs ip, int64_t rbar) {
-  const int wv = threadIdx.x >> 6, lane = lane_id();
-  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
-  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB], TKB = ip.hdr[H_TKB];
-  if (r >= R || r >= rbar) return;
-  int hs, b, qb;
-  row_coords(ip, (int)r, TQB, hs, b, qb);
-  const int base = hs * TKB + ip.kbase[b];
-  for (int e = ip.row_ptr[r] + lane; e < ip.row_ptr[r + 1]; e += 64) atomicAdd(&ip.col_cnt[base + ip.cols[e]], 1);
-}
-
 __global__ __launch_bounds__(256) void k_col_fill(IndexPtrs ip, int64_t rbar) {
   const int wv = threadIdx.x >> 6, lane = lane_id();
   const int64_t r = (int64_t)blockIdx.x * 4 + wv;
