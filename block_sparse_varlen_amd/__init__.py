@@ -35,6 +35,9 @@ BSA_SPARSE_IDX_BATCH_I32, BSA_SPARSE_KV_IDX_I32, BSA_SPARSE_KV_IDX_BATCH_I32 = 4
 BSA_MASK_NONE, BSA_MASK_CAUSAL, BSA_MASK_BAND = 0, 1, 2
 BSA_KV_TND, BSA_KV_PAGED = 0, 1
 BSA_FLAG_INDEX_BUILT, BSA_FLAG_DETERMINISTIC, BSA_FLAG_DQ_ATOMIC = 1, 2, 4
+BSA_FLAG_CHECK_VALUES = 8
+(BSA_CHECK_CU_Q_ENDS, BSA_CHECK_CU_Q_ORDER, BSA_CHECK_SQ_LONG, BSA_CHECK_CU_KV_ENDS, BSA_CHECK_CU_KV_ORDER,
+ BSA_CHECK_SKV_LONG, BSA_CHECK_PAGE) = 1, 2, 4, 8, 16, 32, 64
 (BSA_KERNEL_INDEX, BSA_KERNEL_FWD, BSA_KERNEL_BWD_PRE, BSA_KERNEL_BWD_DKDV, BSA_KERNEL_BWD_DQ) = range(5)
 KERNEL_NAMES = {0: "index", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq"}
 

@@ -83,7 +83,8 @@ bsa_status_t check_problem(const bsa_problem_t* p) {
     if (p->page_stride < (int64_t)p->page_size * row || p->page_stride % row != 0) return BSA_ERR_PARAM_INVALID;
   }
   if (!(p->scale >= 0.0) || !std::isfinite(p->scale)) return BSA_ERR_PARAM_INVALID;
-  if ((p->flags & ~(uint32_t)(BSA_FLAG_INDEX_BUILT | BSA_FLAG_DETERMINISTIC | BSA_FLAG_DQ_ATOMIC)) != 0)
+  if ((p->flags & ~(uint32_t)(BSA_FLAG_INDEX_BUILT | BSA_FLAG_DETERMINISTIC | BSA_FLAG_DQ_ATOMIC |
+                             BSA_FLAG_CHECK_VALUES)) != 0)
     return BSA_ERR_PARAM_INVALID;
   if ((p->flags & BSA_FLAG_DETERMINISTIC) && (p->flags & BSA_FLAG_DQ_ATOMIC)) return BSA_ERR_PARAM_INVALID;
   // valid descriptors without a compiled variant
@@ -295,6 +296,33 @@ bsa_status_t check_index_ptrs(const bsa_problem_t* p, const int64_t* cu_q, const
 
 bsa_status_t from_hip(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_RUNTIME; }
 
+// BSA_FLAG_CHECK_VALUES: checks the device-resident sequence description
+// with one kernel and waits for its word (the one call path that synchronizes
+// the stream), before any kernel that trusts those values is enqueued.
+// block_table may be NULL (index-only calls read no page).
+bsa_status_t check_values(const bsa_problem_t* p, const int64_t* cu_q, const int64_t* cu_kv,
+                          const int32_t* seqused, const int32_t* block_table, int32_t* hdr, hipStream_t s) {
+  const bool paged = p->kv_layout == BSA_KV_PAGED;
+  CheckArgs c{};
+  c.cu_q = cu_q;
+  c.cu_kv = paged ? nullptr : cu_kv;
+  c.seqused_kv = paged ? seqused : nullptr;
+  c.block_table = paged ? block_table : nullptr;
+  c.batch = p->batch;
+  c.max_sq = p->max_seqlen_q;
+  c.max_skv = p->max_seqlen_kv;
+  c.page_size = paged ? p->page_size : 0;
+  c.max_pages = paged ? p->max_pages_per_seq : 0;
+  c.total_q = p->total_q;
+  c.total_kv = p->total_kv;
+  if (launch_check_values(c, hdr, s) != hipSuccess) return BSA_ERR_RUNTIME;
+  int32_t word = -1;
+  if (hipMemcpyAsync(&word, hdr + H_CHECK, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return BSA_ERR_RUNTIME;
+  if (hipStreamSynchronize(s) != hipSuccess) return BSA_ERR_RUNTIME;
+  return word == 0 ? BSA_OK : BSA_ERR_PARAM_INVALID;
+}
+
 // ------------------------------------------------------------- profiling --
 struct ProfRec {
   int kernel;
@@ -356,6 +384,10 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const IndexPtrs ip = make_ptrs(workspace, L, false, row_tiles(p));
+  if (p->flags & BSA_FLAG_CHECK_VALUES) {
+    st = check_values(p, cu_q, cu_kv, seqused, block_table, ip.hdr, s);
+    if (st != BSA_OK) return st;
+  }
   const int group = p->num_heads_q / p->num_heads_kv;
   const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
   hipError_t e = hipSuccess;
@@ -490,6 +522,10 @@ bsa_status_t bsa_build_index(const bsa_problem_t* p, const int64_t* cu_q, const 
   if (ws_bytes < L.total) return BSA_ERR_PARAM_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const IndexPtrs ip = make_ptrs(workspace, L, with_csc != 0, row_tiles(p));
+  if (p->flags & BSA_FLAG_CHECK_VALUES) {
+    st = check_values(p, cu_q, cu_kv, seqused, nullptr, ip.hdr, s);
+    if (st != BSA_OK) return st;
+  }
   prof_begin(BSA_KERNEL_INDEX, s);
   const hipError_t e = launch_index(make_seq(p, cu_q, cu_kv, seqused), make_sel(p, sparse, count, workspace, L, b), b, ip,
                                     p->num_heads_kv, p->num_heads_q / p->num_heads_kv, with_csc != 0, s);
@@ -514,6 +550,8 @@ bsa_status_t bsa_fwd_noalloc(const bsa_problem_t* p, const void* q, const void* 
   // the index of this entry point lives in the library's scratch array, so a
   // prebuilt one cannot be handed in
   if (p->flags & BSA_FLAG_INDEX_BUILT) return BSA_ERR_PARAM_INVALID;
+  // nor can it wait for a value check (its callers may be capturing a graph)
+  if (p->flags & BSA_FLAG_CHECK_VALUES) return BSA_ERR_PARAM_INVALID;
   const Bounds b = make_bounds(p);
   if (!bounds_fit(b)) return BSA_ERR_PARAM_INVALID;
   const size_t need = make_layout(p, b, false, false).total;
@@ -548,6 +586,10 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const IndexPtrs ip = make_ptrs(workspace, L, true, row_tiles(p));
+  if (p->flags & BSA_FLAG_CHECK_VALUES) {
+    st = check_values(p, cu_q, cu_kv, seqused, block_table, ip.hdr, s);
+    if (st != BSA_OK) return st;
+  }
   const int group = p->num_heads_q / p->num_heads_kv;
   const SeqArgs seq = make_seq(p, cu_q, cu_kv, seqused);
   hipError_t e = hipSuccess;

@@ -738,6 +738,51 @@ hipError_t radix_sort(const IndexPtrs& ip, const int32_t* key, const int32_t* va
   return hipGetLastError();
 }
 
+
+// Value check of BSA_FLAG_CHECK_VALUES: one workgroup walks the sequences
+// (and, paged, every block_table entry that a pass would read) and writes the
+// CHK_* bits of the failed checks to hdr[H_CHECK].  Every array is read only
+// inside the extent the descriptor gives it, whatever the values: a page
+// count taken from seqused_kv is clamped to [0, max_pages] first.
+__global__ __launch_bounds__(1024) void k_check_values(CheckArgs c, int32_t* hdr) {
+  __shared__ uint32_t bits;
+  if (threadIdx.x == 0) bits = 0u;
+  __syncthreads();
+  uint32_t m = 0u;
+  if (threadIdx.x == 0) {
+    if (c.cu_q[0] != 0 || c.cu_q[c.batch] != c.total_q) m |= CHK_CU_Q_ENDS;
+    if (c.cu_kv && (c.cu_kv[0] != 0 || c.cu_kv[c.batch] > c.total_kv)) m |= CHK_CU_KV_ENDS;
+  }
+  for (int b = threadIdx.x; b < c.batch; b += blockDim.x) {
+    const int64_t sq = c.cu_q[b + 1] - c.cu_q[b];
+    if (sq < 0) m |= CHK_CU_Q_ORDER;
+    else if (sq > c.max_sq) m |= CHK_SQ_LONG;
+    if (c.cu_kv) {
+      const int64_t skv = c.cu_kv[b + 1] - c.cu_kv[b];
+      if (skv < 0) m |= CHK_CU_KV_ORDER;
+      else if (skv > c.max_skv) m |= CHK_SKV_LONG;
+    } else {
+      const int32_t used = c.seqused_kv[b];
+      if (used < 0 || used > c.max_skv) m |= CHK_SKV_LONG;
+    }
+  }
+  if (c.block_table) {
+    const int64_t n = (int64_t)c.batch * c.max_pages;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const int b = (int)(i / c.max_pages), pg = (int)(i - (int64_t)b * c.max_pages);
+      const int64_t cap = (int64_t)c.max_pages * c.page_size;
+      const int64_t used = c.seqused_kv[b] < 0 ? 0 : (c.seqused_kv[b] > cap ? cap : (int64_t)c.seqused_kv[b]);
+      if (pg < (used + c.page_size - 1) / c.page_size) {
+        const int32_t id = c.block_table[i];
+        if (id < 0 || id >= c.total_kv) m |= CHK_PAGE;
+      }
+    }
+  }
+  if (m) atomicOr(&bits, m);
+  __syncthreads();
+  if (threadIdx.x == 0) hdr[H_CHECK] = (int32_t)bits;
+}
+
 }  // namespace
 
 // Launches: setup, row counts (+ clearing the column counters), row scan,
@@ -792,6 +837,11 @@ hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd
   k_radix_hist2<<<nba + nbb, 256, 0, st>>>(sa, sb);
   k_scan_excl2<<<1, 1024, 0, st>>>(sa.hist, 256 * (int64_t)nba, sb.hist, 256 * (int64_t)nbb);
   k_radix_scatter2<<<nba + nbb, 256, 0, st>>>(sa, sb);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_values(const CheckArgs& c, int32_t* hdr, hipStream_t st) {
+  k_check_values<<<1, 1024, 0, st>>>(c, hdr);
   return hipGetLastError();
 }
 

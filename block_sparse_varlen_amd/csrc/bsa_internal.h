@@ -16,7 +16,31 @@ enum HeaderSlot {
   H_C = 3,      // columns = Hs * TKB
   H_NNZ = 4,    // visited (row, kv-block) pairs
   H_KVITEMS = 5,// N2 * TKB
+  H_CHECK = 6,  // value check word (CHK_* bits) of BSA_FLAG_CHECK_VALUES; 0 once the index is built
   H_COUNT = 16  // header size in int32 (padded)
+};
+
+// Bits of the value check word (the numbers of the public BSA_CHECK_* list).
+enum CheckBit : uint32_t {
+  CHK_CU_Q_ENDS = 1u,    // cu_seqlens_q[0] != 0 or cu_seqlens_q[B] != total_q
+  CHK_CU_Q_ORDER = 2u,   // cu_seqlens_q decreases somewhere
+  CHK_SQ_LONG = 4u,      // some Sq_b > max_seqlen_q
+  CHK_CU_KV_ENDS = 8u,   // TND: cu_seqlens_kv[0] != 0 or cu_seqlens_kv[B] > total_kv
+  CHK_CU_KV_ORDER = 16u, // TND: cu_seqlens_kv decreases somewhere
+  CHK_SKV_LONG = 32u,    // some Skv_b > max_seqlen_kv (TND), or seqused_kv[b] outside [0, max_seqlen_kv] (paged)
+  CHK_PAGE = 64u         // paged: a block_table entry of a page holding keys < seqused_kv[b] outside [0, pages)
+};
+
+// The device-resident sequence description and the extents the descriptor
+// gives each array: cu_q [batch + 1], cu_kv [batch + 1] (TND), seqused_kv
+// [batch] and block_table [batch, max_pages] (paged).
+struct CheckArgs {
+  const int64_t* cu_q;
+  const int64_t* cu_kv;       // TND, else nullptr
+  const int32_t* seqused_kv;  // paged, else nullptr
+  const int32_t* block_table; // paged, else nullptr
+  int32_t batch, max_sq, max_skv, page_size, max_pages;
+  int64_t total_q, total_kv;  // total_kv: rows (TND) or pages (paged)
 };
 
 enum SparseKind { SP_NONE = 0, SP_MASK = 1, SP_SABI = 2, SP_IDX = 3, SP_IDX_B = 4, SP_KV = 5, SP_KV_B = 6 };
@@ -196,6 +220,8 @@ struct BwdArgs {
 // ---- launchers (defined in the .hip files) ----
 hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip,
                         int n2, int group, bool with_csc, hipStream_t stream);
+// writes the value check word of `c` to hdr[H_CHECK]
+hipError_t launch_check_values(const CheckArgs& c, int32_t* hdr, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t grid, hipStream_t stream);
 // e4m3 q / k / v (head dim 128), out in out_dtype
 hipError_t launch_fwd_fp8(const FwdArgs& a, int out_dtype, int64_t grid, hipStream_t stream);

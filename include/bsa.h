@@ -44,7 +44,7 @@
  *
  * Ownership.  Every pointer argument of stage 2 is caller-owned device
  * memory (except the descriptor, a host pointer).  The library never
- * allocates, frees or synchronizes; outputs are fully overwritten (no
+ * allocates, frees or synchronizes (BSA_FLAG_CHECK_VALUES aside); outputs are fully overwritten (no
  * pre-zeroing needed; for paged dK/dV see bsa_bwd) and must not alias inputs
  * or the workspace; workspace
  * contents are undefined on entry and exit.  Calls on different streams with
@@ -52,10 +52,11 @@
  *
  * Errors.  Status codes reuse the pages' numbers (GenericBlockSparseAttention
  * page, first-stage return codes).  Device-resident values (cu_seqlens,
- * seqused_kv, block_table entries) are not validated, as on the pages
- * (GenericBlockSparseAttention page, "values are not checked at tiling
+ * seqused_kv, block_table entries) are not validated by default, as on the
+ * pages (GenericBlockSparseAttention page, "values are not checked at tiling
  * time"): inconsistent values are undefined behaviour, except out-of-range
- * *selection* entries, which are defined as skipped.
+ * *selection* entries, which are defined as skipped.  BSA_FLAG_CHECK_VALUES
+ * validates them first.
  */
 #ifndef BSA_H_
 #define BSA_H_
@@ -150,6 +151,30 @@ enum { BSA_FLAG_INDEX_BUILT = 1u };
  * run to run and so excludes BSA_FLAG_DQ_ATOMIC (both set:
  * BSA_ERR_PARAM_INVALID).  Both flags are ignored by bsa_fwd. */
 enum { BSA_FLAG_DETERMINISTIC = 2u, BSA_FLAG_DQ_ATOMIC = 4u };
+/* BSA_FLAG_CHECK_VALUES: before any other device work, bsa_fwd / bsa_bwd /
+ * bsa_build_index run one validator kernel over the device-resident sequence
+ * description, wait for it (the stream is synchronized: not for use under
+ * graph capture) and return BSA_ERR_PARAM_INVALID, with nothing else
+ * enqueued, when a check fails.  The failed checks' BSA_CHECK_* bits are
+ * left in header[6] of the workspace (bsa_index_view's off_header; 0 after a
+ * call that passed).  Checked: cu_seqlens_q starts at 0, never decreases and
+ * ends at total_q, with every Sq_b <= max_seqlen_q; TND: cu_seqlens_kv starts
+ * at 0, never decreases and ends at most at total_kv, with every Skv_b <=
+ * max_seqlen_kv; paged: every seqused_kv[b] in [0, max_seqlen_kv] and, in
+ * bsa_fwd / bsa_bwd, every block_table entry of a page that holds keys below
+ * seqused_kv[b] in [0, total_kv).  Not checked: whether sequences share a
+ * page (bsa_bwd forbids it) and selection values (out-of-range entries are
+ * defined as skipped).  bsa_fwd_noalloc rejects the flag. */
+enum { BSA_FLAG_CHECK_VALUES = 8u };
+enum {
+  BSA_CHECK_CU_Q_ENDS = 1,    /* cu_seqlens_q[0] != 0 or cu_seqlens_q[B] != total_q */
+  BSA_CHECK_CU_Q_ORDER = 2,   /* cu_seqlens_q decreases somewhere */
+  BSA_CHECK_SQ_LONG = 4,      /* some Sq_b > max_seqlen_q */
+  BSA_CHECK_CU_KV_ENDS = 8,   /* TND: cu_seqlens_kv[0] != 0 or cu_seqlens_kv[B] > total_kv */
+  BSA_CHECK_CU_KV_ORDER = 16, /* TND: cu_seqlens_kv decreases somewhere */
+  BSA_CHECK_SKV_LONG = 32,    /* TND: some Skv_b > max_seqlen_kv; paged: seqused_kv[b] outside [0, max_seqlen_kv] */
+  BSA_CHECK_PAGE = 64         /* paged: a block_table entry that is read lies outside [0, total_kv) */
+};
 
 typedef struct bsa_problem {
   uint32_t struct_size;      /* sizeof(bsa_problem_t) */
@@ -224,7 +249,8 @@ bsa_status_t bsa_fwd(const bsa_problem_t* p, const void* q, const void* k, const
  * and give undefined results; calls ordered on one stream are safe.  Returns
  * BSA_ERR_PARAM_INVALID when the problem's forward workspace
  * (bsa_get_workspace_size's fwd_bytes) exceeds the array or when
- * BSA_FLAG_INDEX_BUILT is set, before any device work.  Allocates nothing
+ * BSA_FLAG_INDEX_BUILT or BSA_FLAG_CHECK_VALUES is set, before any device
+ * work.  Allocates nothing
  * (no hipMalloc / hipFree / allocating library call). */
 #define BSA_NOALLOC_SCRATCH_BYTES (16u << 20)
 bsa_status_t bsa_fwd_noalloc(const bsa_problem_t* p, const void* q, const void* k, const void* v,
@@ -253,7 +279,8 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
  * workspace; bsa_index_view says where each product sits.  Layout (all int32,
  * see the field comments):
  *   header[0..7]: totalQBlocks, totalKBlocks, R = Hs*totalQBlocks rows,
- *                 C = Hs*totalKBlocks columns, nnz, N2*totalKBlocks kv items, 0, 0
+ *                 C = Hs*totalKBlocks columns, nnz, N2*totalKBlocks kv items,
+ *                 0 (the value check word, see BSA_FLAG_CHECK_VALUES), 0
  *   row_ptr[R+1], cols[nnz]: per row r = hs*totalQBlocks + qbase_b + qb the
  *                 ascending local KV blocks holding at least one allowed pair
  *   work[R]:      rows by visited count descending, ties by row id

@@ -63,7 +63,24 @@ def test_dq_flags():
     f2, b2 = bsa.bsa_get_workspace_size(good(flags=bsa.BSA_FLAG_DETERMINISTIC))
     assert (f2, b2) == (f0, b0)
     assert status(good(flags=bsa.BSA_FLAG_DETERMINISTIC | bsa.BSA_FLAG_DQ_ATOMIC)) == bsa.BSA_ERR_PARAM_INVALID
-    assert status(good(flags=8)) == bsa.BSA_ERR_PARAM_INVALID
+    assert status(good(flags=32)) == bsa.BSA_ERR_PARAM_INVALID
+
+
+def test_check_values_flag():
+    """BSA_FLAG_CHECK_VALUES goes with every other flag and leaves the
+    workspace sizes as they are; bsa_fwd_noalloc, which must not wait on the
+    stream, rejects it on the host before any device work (the dummy
+    pointers are never dereferenced)."""
+    f0, b0 = bsa.bsa_get_workspace_size(good())
+    assert bsa.bsa_get_workspace_size(good(flags=bsa.BSA_FLAG_CHECK_VALUES)) == (f0, b0)
+    for extra in (bsa.BSA_FLAG_INDEX_BUILT, bsa.BSA_FLAG_DETERMINISTIC, bsa.BSA_FLAG_DQ_ATOMIC):
+        assert status(good(flags=bsa.BSA_FLAG_CHECK_VALUES | extra)) == bsa.BSA_OK
+    p = good(flags=bsa.BSA_FLAG_CHECK_VALUES)
+    lib = bsa.library()
+    assert lib.bsa_fwd_noalloc(ctypes.byref(p), 1, 1, 1, 1, 1, None, 1, None, None, 1, 1,
+                               None) == bsa.BSA_ERR_PARAM_INVALID
+    assert [bsa.BSA_CHECK_CU_Q_ENDS, bsa.BSA_CHECK_CU_Q_ORDER, bsa.BSA_CHECK_SQ_LONG, bsa.BSA_CHECK_CU_KV_ENDS,
+            bsa.BSA_CHECK_CU_KV_ORDER, bsa.BSA_CHECK_SKV_LONG, bsa.BSA_CHECK_PAGE] == [1, 2, 4, 8, 16, 32, 64]
 
 
 def test_band_mask_accepted():
