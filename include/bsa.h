@@ -48,7 +48,10 @@
  * pre-zeroing needed; for paged dK/dV see bsa_bwd) and must not alias inputs
  * or the workspace; workspace
  * contents are undefined on entry and exit.  Calls on different streams with
- * different workspaces may run concurrently.
+ * different workspaces may run concurrently.  A call enqueues nothing but
+ * kernel launches, so it can be captured into a HIP graph and replayed
+ * (not with BSA_FLAG_CHECK_VALUES, which waits on the stream, nor while
+ * bsa_profile_enable is on).
  *
  * Errors.  Status codes reuse the pages' numbers (GenericBlockSparseAttention
  * page, first-stage return codes).  Device-resident values (cu_seqlens,
