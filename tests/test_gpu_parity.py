@@ -153,6 +153,13 @@ def fwd_cases():
                                      causal=True),
         "tile_idx_bx1_short_rows": _short_idx(R(151, lens_q=[260, 200], N1=2, D=128, kind="idx", bx=1, width=4,
                                                 causal=True), 300),
+        # the descriptor's limits: 256 q-heads (a group of 128 sharing one
+        # pattern, or 256 per-q-head patterns), 4096 x 4096 blocks, top-256 lists
+        "limit_n1_256_group128": R(160, lens_q=[150, 70], N1=256, N2=2, D=64, kind="mask", sparse_heads=2,
+                                   causal=True, density=0.6),
+        "limit_n1_256_perhead_idx": R(161, lens_q=[130], N1=256, D=64, kind="idx", width=2),
+        "limit_bx4096_by4096": R(162, lens_q=[4500, 300], N1=2, D=64, kind="mask", bx=4096, by=4096, density=0.7),
+        "limit_topk256_by16": R(163, lens_q=[260], lens_kv=[4200], N1=2, D=64, kind="idx", by=16, width=256),
     }
 
 
@@ -266,6 +273,11 @@ def bwd_cases():
                                               page_size=64, causal=True),
         "tile_idx_bx32_short_rows_perhead": _short_idx(R(252, lens_q=[600, 400], N1=4, N2=2, D=64, kind="idx",
                                                          sparse_heads=4, bx=32, width=5), 20),
+        "limit_n1_256_group128": R(260, lens_q=[150, 70], N1=256, N2=2, D=64, kind="mask", sparse_heads=2,
+                                   causal=True, density=0.6),
+        "limit_n1_256_perhead_idx": R(261, lens_q=[130], N1=256, D=64, kind="idx", width=2),
+        "limit_bx4096_by4096": R(262, lens_q=[4500, 300], N1=2, D=64, kind="mask", bx=4096, by=4096, density=0.7),
+        "limit_topk256_by16": R(263, lens_q=[260], lens_kv=[4200], N1=2, D=64, kind="idx", by=16, width=256),
     }
 
 
