@@ -123,6 +123,30 @@ int main() {
          "short workspace rejected");
   expect(std::strlen(bsa_status_string(BSA_ERR_INNER)) > 0, "status string");
 
+  // value check: sequence 0 longer than max_seqlen_q / _kv is rejected before
+  // any other work, with its bits in header slot 6; consistent values pass
+  const int64_t cu_bad_host[3] = {0, 320, 470};
+  int64_t* cu_bad;
+  if (!hip_ok(hipMalloc((void**)&cu_bad, sizeof(cu_bad_host)), "malloc cu_bad") ||
+      !hip_ok(hipMemcpy(cu_bad, cu_bad_host, sizeof(cu_bad_host), hipMemcpyHostToDevice), "copy cu_bad"))
+    return 1;
+  bsa_problem_t pc = p;
+  pc.flags = BSA_FLAG_CHECK_VALUES;
+  expect(bsa_fwd(&pc, q, k, v, cu_bad, cu_bad, nullptr, nullptr, nullptr, nullptr, out, lse, ws, bwd_bytes,
+                 nullptr) == BSA_ERR_PARAM_INVALID,
+         "value check rejects a sequence past max_seqlen");
+  bsa_index_view_t view;
+  expect(bsa_index_view(&pc, 0, &view) == BSA_OK, "index view");
+  int32_t word = 0;
+  hip_ok(hipMemcpy(&word, static_cast<char*>(ws) + view.off_header + 6 * sizeof(int32_t), sizeof(word),
+                   hipMemcpyDeviceToHost),
+         "copy check word");
+  expect(word == (BSA_CHECK_SQ_LONG | BSA_CHECK_SKV_LONG), "check word names both long sequences");
+  expect(bsa_fwd(&pc, q, k, v, cu, cu, nullptr, nullptr, nullptr, nullptr, out, lse, ws, bwd_bytes, nullptr) ==
+             BSA_OK,
+         "value check passes consistent values");
+  hipFree(cu_bad);
+
   // forward: O = 1, lse finite
   expect(bsa_fwd(&p, q, k, v, cu, cu, nullptr, nullptr, nullptr, nullptr, out, lse, ws, bwd_bytes, nullptr) == BSA_OK,
          "bsa_fwd");
