@@ -739,6 +739,27 @@ def test_lse_merge_of_disjoint_block_sets():
     np.testing.assert_allclose(mix[fin], O[fin], rtol=0, atol=1e-12)
 
 
+def test_context_parallel_shards_as_band_masks():
+    """Causal shards of one sequence (queries [qs, qs + nq) against keys
+    [ks, ks + nk)) with the band offsets of tests/cp_shards.py give the whole
+    sequence's rows: in full when the shard holds every key its rows reach,
+    and through the LSE merge when the keys are split over shards."""
+    import cp_shards
+    case = synth.random_case(81, lens_q=[150], lens_kv=[190], N1=2, D=8, bx=16, by=16, kind="none", causal=True)
+    O, lse = oracle.forward(case)
+    for qs, nq, ks, nk in ((0, 70, 0, 190), (70, 80, 0, 190), (30, 60, 0, 150)):
+        Os, ls = oracle.forward(cp_shards.shard(case, qs, nq, ks, nk))
+        np.testing.assert_allclose(Os, O[qs:qs + nq], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ls, lse[qs:qs + nq], rtol=0, atol=1e-12)
+    # rows 80..149 against keys [0, 95) and [95, 190), merged
+    parts = [oracle.forward(cp_shards.shard(case, 80, 70, ks, nk)) for ks, nk in ((0, 95), (95, 95))]
+    Om, lm = cp_shards.merge(parts)
+    np.testing.assert_allclose(Om, O[80:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, lse[80:], rtol=0, atol=1e-12)
+    # a negative nextTokens: the first shard's window ends below its diagonal
+    assert cp_shards.next_tokens(case, 0, 70, 0, 190) < 0
+
+
 def test_config_structures():
     """Structural facts of the benchmark workloads: exact visited-pair count
     of the long-context mask and shapes of the other selection tensors."""
