@@ -423,6 +423,26 @@ def test_bwd_small(name):
     check_bwd(case, dc, tag=name)
 
 
+@pytest.mark.parametrize("paged", [False, True], ids=["tnd", "paged"])
+def test_bwd_without_queries_zeroes_key_gradients(paged):
+    """Every sequence with keys but no queries (T_q = 0): the forward is a
+    no-op, and the backward writes dK = dV = 0 at every key below Skv_b (no row
+    attends them), leaving the rest of a page pool as it was."""
+    case = synth.random_case(160 + int(paged), lens_q=[0, 0], lens_kv=[300, 200], N1=4, N2=2, D=64, kind="mask",
+                             paged=paged, page_size=128)
+    say(f"bwd without queries ({'paged' if paged else 'tnd'})")
+    dc = DeviceCase(case, with_bwd=True)
+    dc.fwd()
+    nan_fill(dc.dk, dc.dv)
+    dc.bwd()
+    torch.cuda.synchronize()
+    dk = dc.dk.float().cpu().numpy()
+    dv = dc.dv.float().cpu().numpy()
+    val = kv_valid(case)
+    assert np.all(dk[val] == 0) and np.all(dv[val] == 0)
+    assert np.all(np.isnan(dk[~val])) and np.all(np.isnan(dv[~val]))
+
+
 @pytest.mark.parametrize("name", ["mask_gqa_shared_causal", "idx_perhead_gqa", "tile_idx_bx1_gqa_causal"])
 def test_bwd_deterministic(name):
     case = BWD[name]
