@@ -34,19 +34,22 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
   constexpr int CH = D / 8;
   const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / CH;
   const int c = threadIdx.x % CH;
-  float acc = 0.f;
-  if (row < a.rows) {
-    const u32x4_t o = gload16(reinterpret_cast<const uint16_t*>(a.out) + row * D + c * 8);
-    const u32x4_t d = gload16(reinterpret_cast<const uint16_t*>(a.dout) + row * D + c * 8);
-    acc = MF::lo(o.x) * MF::lo(d.x) + MF::hi(o.x) * MF::hi(d.x) + MF::lo(o.y) * MF::lo(d.y) +
-          MF::hi(o.y) * MF::hi(d.y) + MF::lo(o.z) * MF::lo(d.z) + MF::hi(o.z) * MF::hi(d.z) +
-          MF::lo(o.w) * MF::lo(d.w) + MF::hi(o.w) * MF::hi(d.w);
-  }
+  // Every lane issues its three loads up front, unconditionally (lanes past
+  // the last row read row 0), so they are in flight together instead of the
+  // second waiting behind the first.
+  const int64_t rr = row < a.rows ? row : 0;
+  const u32x4_t o = gload16(reinterpret_cast<const uint16_t*>(a.out) + rr * D + c * 8);
+  const u32x4_t d = gload16(reinterpret_cast<const uint16_t*>(a.dout) + rr * D + c * 8);
+  float l = a.lse[rr];
+  pin(l);
+  float acc = MF::lo(o.x) * MF::lo(d.x) + MF::hi(o.x) * MF::hi(d.x) + MF::lo(o.y) * MF::lo(d.y) +
+              MF::hi(o.y) * MF::hi(d.y) + MF::lo(o.z) * MF::lo(d.z) + MF::hi(o.z) * MF::hi(d.z) +
+              MF::lo(o.w) * MF::lo(d.w) + MF::hi(o.w) * MF::hi(d.w);
 #pragma unroll
   for (int m = CH / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if (row < a.rows && c == 0) {
     a.ndl[row] = -acc;
-    a.lse2[row] = a.lse[row] * LOG2E;
+    a.lse2[row] = l * LOG2E;
   }
   if (a.dq_acc && row < a.rows) {  // clear this chunk of the atomic dQ accumulator
     float4* z = reinterpret_cast<float4*>(a.dq_acc + row * D + c * 8);
