@@ -49,8 +49,20 @@ bsa_status_t scratch_ptr(void** out) {
 namespace {
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-// grid sizes are padded to whole XCD rounds (see xcd_item in bsa_attn.h)
-int64_t xcd_grid(int64_t items) { return cdiv64(items, NUM_XCD * XCD_SEG) * (NUM_XCD * XCD_SEG); }
+// grid sizes are padded to whole XCD rounds of 8 runs of 2^seg items (see
+// xcd_item in bsa_attn.h)
+int64_t xcd_grid(int64_t items, int seg) {
+  const int64_t round = (int64_t)NUM_XCD << seg;
+  return cdiv64(items, round) * round;
+}
+// XCD run lengths (log2).  Q-major launches (forward, dQ) keep runs of 32
+// neighbouring q-blocks on one XCD, so they share K/V tiles in its L2, unless
+// there are at most ~4 items per workgroup slot (2048 on 256 CUs at two
+// workgroups each): then balance matters more than sharing and runs of 4
+// spread the longest items over the XCDs.  The dK/dV items of one run share
+// few Q/dO tiles, so they always take runs of 4.
+int q_xseg(int64_t items) { return items <= 2048 ? 2 : 5; }
+constexpr int KV_XSEG = 2;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- checks --
@@ -424,8 +436,10 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
   a.page_stride = p->kv_layout == BSA_KV_PAGED ? p->page_stride : 0;
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
+  const int64_t items = b.rbar * a.heads_per_row * cdiv64(item_rows(p), 128);
+  a.xseg = q_xseg(items);
   prof_begin(BSA_KERNEL_FWD, s);
-  const int64_t grid = xcd_grid(b.rbar * a.heads_per_row * cdiv64(item_rows(p), 128));
+  const int64_t grid = xcd_grid(items, a.xseg);
   e = p->dtype == BSA_DTYPE_FP8_E4M3 ? launch_fwd_fp8(a, p->out_dtype, grid, s)
                                      : launch_fwd(a, p->dtype, p->head_dim, grid, s);
   prof_end(BSA_KERNEL_FWD, s);
@@ -649,9 +663,13 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.sub_tiles = (p->block_y + 127) / 128;
   a.sigma = sigma_of(p);
   a.sigma_log2e = a.sigma * 1.4426950408889634f;
+  const int64_t q_items = b.rbar * a.heads_per_row * cdiv64(item_rows(p), 128);
+  const int64_t kv_items = b.kvbar * a.sub_tiles;
+  a.xseg_q = q_xseg(q_items);
+  a.xseg_kv = KV_XSEG;
   if (p->total_kv > 0) {
     prof_begin(BSA_KERNEL_BWD_DKDV, s);
-    e = launch_bwd_dkdv(a, p->dtype, p->head_dim, xcd_grid(b.kvbar * a.sub_tiles), s);
+    e = launch_bwd_dkdv(a, p->dtype, p->head_dim, xcd_grid(kv_items, a.xseg_kv), s);
     prof_end(BSA_KERNEL_BWD_DKDV, s);
     if (e != hipSuccess) return BSA_ERR_RUNTIME;
   }
@@ -660,7 +678,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
     if (acc)
       e = launch_dq_convert(acc, dq, p->total_q * p->num_heads_q * p->head_dim, a.sigma, p->dtype, s);
     else
-      e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(b.rbar * a.heads_per_row * cdiv64(item_rows(p), 128)), s);
+      e = launch_bwd_dq(a, p->dtype, p->head_dim, xcd_grid(q_items, a.xseg_q), s);
     prof_end(BSA_KERNEL_BWD_DQ, s);
   }
   return from_hip(e);

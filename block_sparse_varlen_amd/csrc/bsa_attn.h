@@ -13,14 +13,14 @@ constexpr int QT = 128;  // query rows per Q-major work item (4 waves x 32)
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  xcd_item maps dispatch index `bid` to a work item so that every XCD
-// takes runs of XCD_SEG consecutive items from the longest-first order --
+// takes runs of 2^seg consecutive items from the longest-first order --
 // neighbouring q-blocks (or KV blocks) of one head, which share most of the
 // tiles they read -- while the order across XCDs stays longest-first at a
-// granularity of 8 * XCD_SEG items.  Grids are padded to a multiple of
-// 8 * XCD_SEG; items past the end exit.
-__device__ __forceinline__ int64_t xcd_item(int64_t bid) {
+// granularity of 8 * 2^seg items.  Grids are padded to a multiple of
+// 8 * 2^seg; items past the end exit.
+__device__ __forceinline__ int64_t xcd_item(int64_t bid, int seg) {
   const int64_t x = bid % NUM_XCD, k = bid / NUM_XCD;
-  return (k / XCD_SEG) * (NUM_XCD * XCD_SEG) + x * XCD_SEG + (k % XCD_SEG);
+  return (((k >> seg) * NUM_XCD + x) << seg) + (k & ((1 << seg) - 1));
 }
 
 // A Q-major work item: a slice of at most 128 rows of one q-block of one

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];  // double buffer
 
   QItem it;
-  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
+  if (!decode_qitem(xcd_item(blockIdx.x, a.xseg_q), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row,
+                   a.group, it))
     return;
   const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int my_local = wv * 32 + (lane & 31);
@@ -338,7 +339,7 @@ __global__ __launch_bounds__((64 * DkdvShape<D, DQA>::NW), 1) void k_bwd_dkdv(Bw
   __shared__ __attribute__((aligned(16))) char smem[DKDV_STAGES * STAGE + (DQA ? KT_BYTES + 2 * DS_BYTES : 0)];
 
   const int KVI = ldu(a.hdr, H_KVITEMS);
-  const int64_t flat = xcd_item(blockIdx.x);
+  const int64_t flat = xcd_item(blockIdx.x, a.xseg_kv);
   const int64_t item = flat / a.sub_tiles;
   const int sub = (int)(flat - item * a.sub_tiles);
   if (item >= KVI) return;

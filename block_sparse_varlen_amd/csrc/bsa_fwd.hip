@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   QItem it;
-  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
+  if (!decode_qitem(xcd_item(blockIdx.x, a.xseg), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group,
+                   it))
     return;
   const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int my_local = wv * 32 + (lane & 31);  // row within the item

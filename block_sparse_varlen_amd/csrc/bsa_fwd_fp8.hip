@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   QItem it;
-  if (!decode_qitem(xcd_item(blockIdx.x), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group, it))
+  if (!decode_qitem(xcd_item(blockIdx.x, a.xseg), a.hdr, a.work, a.qb_seq, a.qbase, a.seq, a.heads_per_row, a.group,
+                   it))
     return;
   const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;                    // lane half

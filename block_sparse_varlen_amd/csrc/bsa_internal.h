@@ -53,10 +53,10 @@ constexpr int ROW_TILE = 128;
 constexpr int ROW_TILE_MAX_BX = 32;
 constexpr int ROW_TILE_MAX_KB = 2048;
 
-// Attention work items are handed to the 8 XCDs in runs of XCD_SEG
-// consecutive items (xcd_item in bsa_attn.h); grids are padded to whole rounds.
+// Attention work items are handed to the 8 XCDs in runs of 2^xseg
+// consecutive items (xcd_item in bsa_attn.h; xseg is a launch argument);
+// grids are padded to whole rounds of 8 runs.
 constexpr int NUM_XCD = 8;
-constexpr int XCD_SEG = 32;
 
 // Host-known upper bounds that size every workspace region.
 struct Bounds {
@@ -170,6 +170,7 @@ struct FwdArgs {
   int64_t page_stride;     // elements
   float sigma;             // fp32 scale
   float sigma_log2e;       // scale * log2(e)
+  int32_t xseg;            // log2 of the run of consecutive items each XCD takes
 };
 
 struct BwdPreArgs {
@@ -215,6 +216,7 @@ struct BwdArgs {
   int32_t sub_tiles;       // ceil(block_y / 128): dK/dV tiles per KV block (the last one may be partial)
   float sigma;
   float sigma_log2e;
+  int32_t xseg_q, xseg_kv;  // log2 of the XCD runs of the dQ and the dK/dV launches
 };
 
 // ---- launchers (defined in the .hip files) ----
