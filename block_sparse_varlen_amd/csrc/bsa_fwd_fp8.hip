@@ -159,7 +159,12 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
     more = ld.valid();
     if (more) issue(stage ^ 1, std::false_type{});
     settle_scalar_loads();
-    if (!wave_active || rm == 0u) {  // (row tiles: no row of this wave selects the sub-tile's block)
+    const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
+    // a wave leaves out sub-tiles that no row of it may attend: all keys past
+    // its last row's window end or before its first row's window start (their
+    // scores would all be masked, so nothing changes), and with row tiles the
+    // blocks no row of it selects
+    if (!wave_active || rm == 0u || (WIN && key0 > rw0 + 31 + win_hi) || (LO && key0 + KT - 1 < rw0 + win_lo)) {
       stage ^= 1;
       continue;
     }
@@ -184,7 +189,6 @@ __global__ __launch_bounds__(256, 3) void k_fwd_fp8(FwdArgs a) {
       s[1] = mfma_f8(kop[1][1], qf[1], s[1]);
     }
     // ---- masks: keys past Skv, outside the rows' windows (edge sub-tiles only) ----
-    const int rw0 = it.row_lo + wv * 32 + qoff;  // this wave's first row, shifted to its diagonal key
     const bool edge = key0 + KT > it.skv || gm != 0xFu || rm != 0xFFFFFFFFu ||
                       (WIN && key0 + KT - 1 > rw0 + win_hi) || (LO && key0 < rw0 + 31 + win_lo);
     if (edge) {
