@@ -124,6 +124,24 @@ bool row_tiles(const bsa_problem_t* p) {
 // query rows per q-block of the index and of the work items
 int32_t item_rows(const bsa_problem_t* p) { return row_tiles(p) ? ROW_TILE : p->block_x; }
 
+// Sparse heads per dispatch chunk of the forward and dQ passes.  Rows whose
+// K/V are read at random (sparse selections over long sequences) re-read
+// them from memory many times; when the K/V of all heads exceed the 256 MiB
+// last-level cache, the Q-major passes take their rows head chunk by head
+// chunk (longest-first inside each chunk), the largest power-of-two number
+// of heads whose K/V fit in that cache, so the re-reads hit it.  Returns
+// sparse_heads (one chunk) otherwise.
+int32_t q_chunk_heads(const bsa_problem_t* p) {
+  constexpr int64_t kLastLevelCache = 256ll << 20;
+  const int64_t tokens = p->kv_layout == BSA_KV_PAGED ? p->total_kv * p->page_size : p->total_kv;
+  const int64_t elem = p->dtype == BSA_DTYPE_FP8_E4M3 ? 1 : 2;
+  const int64_t per_head = tokens * p->num_heads_kv * p->head_dim * 2 * elem / std::max(p->sparse_heads, 1);
+  if (per_head <= 0) return std::max(p->sparse_heads, 1);
+  int64_t fit = kLastLevelCache / per_head, c = 1;
+  while (c * 2 <= fit) c *= 2;
+  return (int32_t)std::min<int64_t>(c, std::max(p->sparse_heads, 1));
+}
+
 Bounds make_bounds(const bsa_problem_t* p) {
   Bounds b{};
   const int64_t B = p->batch;
@@ -150,6 +168,7 @@ Bounds make_bounds(const bsa_problem_t* p) {
   b.kvbar = (int64_t)p->num_heads_kv * b.kbar;
   const int group = p->num_heads_q / p->num_heads_kv;
   b.kvkey_max = (p->sparse_heads == p->num_heads_q ? group : 1) * std::max<int32_t>(b.nqb_max, 1);
+  b.q_chunk_heads = q_chunk_heads(p);
   return b;
 }
 
@@ -194,6 +213,7 @@ Layout make_layout(const bsa_problem_t* p, const Bounds& b, bool with_csc, bool 
   // one radix sort's histograms, or both work lists' side by side
   L.hist = take((size_t)(256 * (cdiv64(b.rbar, 256) + cdiv64(b.kvbar, 256)) + 2) * 4);
   L.work = take((size_t)b.rbar * 4);
+  L.work_q = take((size_t)b.rbar * 4);
   // per-KV-block lists are scattered into per-row bitmaps first (rows of
   // selection q-blocks)
   L.kvbm = kv_lists(p->sparse_kind) ? take((size_t)p->sparse_heads * b.qbar_sel * kv_words(b) * 4) : 0;
@@ -239,6 +259,7 @@ IndexPtrs make_ptrs(void* ws, const Layout& L, bool with_csc, bool tiles) {
   ip.val1 = at(L.val1);
   ip.hist = at(L.hist);
   ip.work = at(L.work);
+  ip.work_q = at(L.work_q);
   if (with_csc) {
     ip.col_cnt = at(L.col_cnt);
     ip.col_ptr = at(L.col_ptr);
@@ -423,7 +444,7 @@ bsa_status_t fwd_impl(const bsa_problem_t* p, const void* q, const void* k, cons
   a.qbase = ip.qbase;
   a.row_ptr = ip.row_ptr;
   a.cols = ip.cols;
-  a.work = ip.work;
+  a.work = b.q_chunk_heads < p->sparse_heads ? ip.work_q : ip.work;
   // row tiles without a selection need no row masks: a row's token window
   // already removes every block its own q-block does not visit
   a.row_mask = p->sparse_kind != BSA_SPARSE_NONE ? ip.row_mask : nullptr;
@@ -645,7 +666,7 @@ bsa_status_t bsa_bwd(const bsa_problem_t* p, const void* q, const void* k, const
   a.kbase = ip.kbase;
   a.row_ptr = ip.row_ptr;
   a.cols = ip.cols;
-  a.work = ip.work;
+  a.work = b.q_chunk_heads < p->sparse_heads ? ip.work_q : ip.work;  // the dQ pass's row order
   a.col_ptr = ip.col_ptr;
   a.qrows = ip.qrows;
   a.work_kv = ip.work_kv;

@@ -785,12 +785,26 @@ __global__ __launch_bounds__(1024) void k_check_values(CheckArgs c, int32_t* hdr
 
 }  // namespace
 
+namespace {
+
+// Sort keys of the chunked dispatch order: work entry i gets the head chunk
+// of its row (rows past the last one sort last), so a stable sort groups the
+// longest-first order by chunk.
+__global__ __launch_bounds__(256) void k_chunk_keys(IndexPtrs ip, int64_t rbar, int chunk, int nchunks) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rbar) return;
+  const int R = ip.hdr[H_R], TQB = ip.hdr[H_TQB];
+  const int r = ip.work[i];
+  ip.key0[i] = i < R ? (r / TQB) / chunk : nchunks;
+  ip.val0[i] = r;
+}
+
 // Launches: setup, row counts (+ clearing the column counters), row scan,
 // row fill (+ column counts), then either both work lists at the end with one
 // shared hist / scan / scatter launch each (when both sort in one radix pass)
 // or each list with its own passes.
-hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip, int n2,
-                        int group, bool with_csc, hipStream_t st) {
+hipError_t index_lists(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip, int n2,
+                       int group, bool with_csc, hipStream_t st) {
   const bool merged = with_csc && radix_passes((int64_t)bd.cmax + 1) == 1 &&
                       radix_passes((int64_t)bd.kvkey_max + 1) == 1;
   const bool kv = kv_lists(sel.kind);
@@ -838,6 +852,20 @@ hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd
   k_scan_excl2<<<1, 1024, 0, st>>>(sa.hist, 256 * (int64_t)nba, sb.hist, 256 * (int64_t)nbb);
   k_radix_scatter2<<<nba + nbb, 256, 0, st>>>(sa, sb);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// The block index, then, when the Q-major passes run in head chunks, their
+// dispatch order work_q: work stably sorted by head chunk (key0 / val0 and
+// the sort scratch are free once the lists are built).
+hipError_t launch_index(const SeqArgs& seq, const SelArgs& sel, const Bounds& bd, const IndexPtrs& ip, int n2,
+                        int group, bool with_csc, hipStream_t st) {
+  hipError_t e = index_lists(seq, sel, bd, ip, n2, group, with_csc, st);
+  if (e != hipSuccess || bd.q_chunk_heads >= sel.hs) return e;
+  const int nchunks = (sel.hs + bd.q_chunk_heads - 1) / bd.q_chunk_heads;
+  k_chunk_keys<<<blocks_for(bd.rbar, 256), 256, 0, st>>>(ip, bd.rbar, bd.q_chunk_heads, nchunks);
+  return radix_sort(ip, ip.key0, ip.val0, bd.rbar, nchunks, ip.work_q, st);
 }
 
 hipError_t launch_check_values(const CheckArgs& c, int32_t* hdr, hipStream_t st) {

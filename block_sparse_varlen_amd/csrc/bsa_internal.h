@@ -71,12 +71,13 @@ struct Bounds {
   int32_t cmax;      // largest possible visited count of a row
   int64_t qbar_sel;  // >= total selection q-blocks (block_x rows each; = qbar without row tiles)
   int32_t kvkey_max; // largest possible key of a dK/dV item
+  int32_t q_chunk_heads;  // sparse heads per dispatch chunk of the Q-major passes (>= Hs: one chunk)
 };
 
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct Layout {
   size_t hdr, sq, skv, qbase, kbase, qb_seq, kb_seq;
-  size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work, kvbm;
+  size_t row_cnt, row_ptr, cols, key0, val0, key1, val1, hist, work, work_q, kvbm;
   size_t col_cnt, col_ptr, col_fill, qrows, kvkey0, kvval0, kvkey1, kvval1, kvhist, work_kv;
   size_t ndl, lse2, dq_acc;
   size_t qbase_sel, row_mask, col_mask;  // row tiles only (0 otherwise)
@@ -137,6 +138,7 @@ struct IndexPtrs {
   int32_t* key0; int32_t* val0; int32_t* key1; int32_t* val1;  // [max(rbar, kvbar)]
   int32_t* hist;     // [256 * (ceil(rbar/256) + ceil(kvbar/256)) + 2]
   int32_t* work;     // [rbar]
+  int32_t* work_q;   // [rbar] work grouped by head chunk (the Q-major dispatch order when chunked)
   int32_t* col_cnt;  // [cbar]
   int32_t* col_ptr;  // [cbar+1]
   int32_t* col_fill; // [cbar]
